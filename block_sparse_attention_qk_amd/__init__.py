@@ -1,0 +1,218 @@
+"""MiniMax Sparse Attention (MSA) training hot path on MI355X (gfx950).
+
+Thin Python binding of ``libmsa.so``, whose C ABI is declared in
+``include/msa.h``.  The binding only marshals arguments: it checks tensor
+dtypes, devices and shapes, sizes the caller-owned workspace with
+``torch.empty`` and passes raw device pointers and the current HIP stream.
+Every step of the path runs in the library's HIP kernels; there is no
+fallback.  Importing this module needs the built library (``build.py``); a
+missing library raises ``MsaError`` on first use.
+
+Entry points (same names as the C ABI):
+  msa_proxy_select(qp, kp, topk)               -> idx            (Index Branch)
+  msa_fwd(q, k, v, idx, scale=0.0)             -> (o, lse)       (Main Branch forward)
+  msa_bwd(q, k, v, o, dout, lse, idx, scale)   -> (dq, dk, dv)   (Main Branch backward)
+Layouts: qp, kp [B,T,G,dp] bf16; q, o, dout [B,T,H,d] bf16; k, v [B,T,G,d] bf16;
+idx [B,G,T,topk] int32; lse [B,T,H] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
+    "msa_proxy_select", "msa_fwd", "msa_bwd", "OP_SELECT", "OP_FWD", "OP_BWD", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmsa.so")
+_lib = None
+
+OP_SELECT, OP_FWD, OP_BWD = 0, 1, 2
+EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_fwd",
+                    "msa_bwd", "msa_status_str", "msa_version")
+
+
+class MsaError(RuntimeError):
+    """Raised for a non-zero msa_status or a missing library."""
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dp", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libmsa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MsaError("libmsa.so is not built (%s); run block_sparse_attention_qk_amd/build.py" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, D, SZ, I = ctypes.c_void_p, ctypes.POINTER(_Dims), ctypes.c_size_t, ctypes.c_int
+    lib.msa_workspace_bytes.argtypes = [D, I]
+    lib.msa_workspace_bytes.restype = SZ
+    lib.msa_workspace_min_bytes.argtypes = [D, I]
+    lib.msa_workspace_min_bytes.restype = SZ
+    lib.msa_proxy_select.argtypes = [D, P, P, P, P, SZ, P]
+    lib.msa_fwd.argtypes = [D, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    for f in ("msa_proxy_select", "msa_fwd", "msa_bwd"):
+        getattr(lib, f).restype = I
+    lib.msa_status_str.argtypes = [I]
+    lib.msa_status_str.restype = ctypes.c_char_p
+    lib.msa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _dims(B, T, H, G, d, dp, topk, scale) -> _Dims:
+    return _Dims(int(B), int(T), int(H), int(G), int(d), int(dp), int(topk), float(scale))
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MsaError("libmsa error %d: %s" % (rc, load().msa_status_str(rc).decode()))
+
+
+def msa_workspace_bytes(B, T, H, G, d, dp, topk, op, scale: float = 0.0) -> int:
+    return int(load().msa_workspace_bytes(ctypes.byref(_dims(B, T, H, G, d, dp, topk, scale)), op))
+
+
+def msa_workspace_min_bytes(B, T, H, G, d, dp, topk, op, scale: float = 0.0) -> int:
+    return int(load().msa_workspace_min_bytes(ctypes.byref(_dims(B, T, H, G, d, dp, topk, scale)), op))
+
+
+class Workspace:
+    """Device scratch buffer that grows on demand (owned by the caller)."""
+
+    def __init__(self, device=None, nbytes: int = 0):
+        self.device = torch.device(device) if device is not None else torch.device("cuda")
+        self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
+        if nbytes:
+            self.get(nbytes)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ws(ws: Optional[Workspace], device, nbytes: int) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+    return ws.get(nbytes)
+
+
+def msa_proxy_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, ws: Optional[Workspace] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index Branch: block-index cache idx [B,G,T,topk] int32 (ascending, -1 padded)."""
+    _need(qp, "qp", torch.bfloat16, 4)
+    _need(kp, "kp", torch.bfloat16, 4)
+    if qp.shape != kp.shape:
+        raise ValueError("qp and kp shapes differ: %s vs %s" % (tuple(qp.shape), tuple(kp.shape)))
+    B, T, G, dp = qp.shape
+    dims = _dims(B, T, G, G, 64, dp, topk, 0.0)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_SELECT)
+    if nbytes == 0:
+        _check(2)
+    idx = out if out is not None else torch.empty((B, G, T, topk), dtype=torch.int32, device=qp.device)
+    _need(idx, "idx", torch.int32, 4)
+    w = _ws(ws, qp.device, nbytes)
+    _check(lib.msa_proxy_select(ctypes.byref(dims), _ptr(qp), _ptr(kp), _ptr(idx), _ptr(w), w.numel(),
+                                _stream(qp.device)))
+    return idx
+
+
+def _main_dims(q, k, idx, scale) -> Tuple[_Dims, int, int, int, int, int, int]:
+    B, T, H, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != T or k.shape[3] != d:
+        raise ValueError("k shape %s does not match q shape %s" % (tuple(k.shape), tuple(q.shape)))
+    G = k.shape[2]
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (B, G, T):
+        raise ValueError("idx shape %s does not match [B,G,T,topk] = [%d,%d,%d,*]" % (tuple(idx.shape), B, G, T))
+    topk = idx.shape[3]
+    return _dims(B, T, H, G, d, 32, topk, scale), B, T, H, G, d, topk
+
+
+def msa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, scale: float = 0.0,
+            ws: Optional[Workspace] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Main Branch forward: (o [B,T,H,d] bf16, lse [B,T,H] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(idx, "idx", torch.int32, 4)
+    if v.shape != k.shape:
+        raise ValueError("v shape %s differs from k shape %s" % (tuple(v.shape), tuple(k.shape)))
+    dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_FWD)
+    if nbytes == 0:
+        _check(2)
+    if out is None:
+        o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    w = _ws(ws, q.device, nbytes)
+    _check(lib.msa_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), _ptr(w),
+                       w.numel(), _stream(q.device)))
+    return o, lse
+
+
+def msa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+            lse: torch.Tensor, idx: torch.Tensor, scale: float = 0.0, ws: Optional[Workspace] = None,
+            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Main Branch backward of sum(o * dout): (dq, dk, dv) in bf16."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(idx, "idx", torch.int32, 4)
+    if v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or lse.shape != q.shape[:3]:
+        raise ValueError("inconsistent shapes for msa_bwd")
+    dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_BWD)
+    if nbytes == 0:
+        _check(2)
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    w = _ws(ws, q.device, nbytes)
+    _check(lib.msa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(idx),
+                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
+    return dq, dk, dv

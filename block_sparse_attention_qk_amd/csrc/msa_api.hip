@@ -1,0 +1,250 @@
+// C ABI of libmsa (declared in include/msa.h): host-side argument checks,
+// workspace layout, the walk over token windows, and the kernel chain of each
+// entry point on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int BWD_ITEM_TOKENS = 1 << 30;  // one backward item per (batch, group, block)
+constexpr size_t CAP_SELECT = (size_t)8 << 30;
+constexpr size_t CAP_MAIN = (size_t)40 << 30;
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  int W = 0;
+  size_t total = 0;
+  size_t pooled = 0;
+  size_t counts = 0, base = 0, len = 0, items = 0, item_count = 0, list = 0;
+  int max_items = 0;
+  size_t part_o = 0, part_lse = 0;
+  size_t Dd = 0, dk_acc = 0, dv_acc = 0, dq_part = 0;
+};
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = up(off + bytes);
+    return o;
+  }
+};
+
+void carve_inverse(Layout& L, Carver& c, const Geo& g, int W, int item_tokens) {
+  const size_t BG = (size_t)g.B * g.G;
+  const size_t nchunk = (W + INV_CHUNK - 1) / INV_CHUNK;
+  L.max_items = inv_max_items(g, W, item_tokens);
+  L.counts = c.take(BG * nchunk * g.N * 4);
+  L.base = c.take(BG * g.N * 4);
+  L.len = c.take(BG * g.N * 4);
+  L.items = c.take(BG * (size_t)L.max_items * 16);
+  L.item_count = c.take(BG * 4);
+  L.list = c.take(BG * (size_t)W * g.K * 4);
+}
+
+Layout layout(const Geo& g, msa_op op, int W) {
+  Layout L;
+  L.W = W;
+  Carver c;
+  const size_t BG = (size_t)g.B * g.G;
+  const size_t pairs = BG * (size_t)W * g.K;
+  if (op == MSA_OP_SELECT) {
+    L.pooled = c.take(BG * (size_t)W * g.N * 4);
+  } else if (op == MSA_OP_FWD) {
+    carve_inverse(L, c, g, W, FWD_ITEM_TOKENS);
+    L.part_o = c.take(pairs * g.R * g.D * 2);
+    L.part_lse = c.take(pairs * g.R * 4);
+  } else {
+    const size_t kv = (size_t)g.B * g.T * g.G * g.D;
+    L.Dd = c.take((size_t)g.B * g.T * g.H * 4);
+    L.dk_acc = c.take(kv * 4);
+    L.dv_acc = c.take(kv * 4);
+    carve_inverse(L, c, g, W, BWD_ITEM_TOKENS);
+    L.dq_part = c.take(pairs * g.R * g.D * 2);
+  }
+  L.total = c.off;
+  return L;
+}
+
+// Window lengths are T itself or multiples of 256 tokens.
+int min_window(const Geo& g) { return g.T < 256 ? g.T : 256; }
+
+// Largest window whose layout fits in `bytes`; 0 if none does.
+int fit_window(const Geo& g, msa_op op, size_t bytes) {
+  if (layout(g, op, g.T).total <= bytes) return g.T;
+  int lo = 0, hi = (g.T - 1) / 256;  // candidate windows 256 * m, m in [1, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (layout(g, op, 256 * mid).total <= bytes) lo = mid; else hi = mid - 1;
+  }
+  if (lo == 0) return layout(g, op, min_window(g)).total <= bytes ? min_window(g) : 0;
+  return 256 * lo;
+}
+
+bool is_pow2_le16(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
+
+msa_status make_geo(const msa_dims* d, msa_op op, Geo* g) {
+  if (!d) return MSA_ERR_NULL;
+  if (d->B < 1 || d->T < 128 || d->T % 128 != 0 || d->T > (1 << 20) || d->G < 1 || d->topk < 1 ||
+      d->topk > 1024 || std::isnan(d->scale))
+    return MSA_ERR_SHAPE;
+  if ((int64_t)d->T * d->topk >= ((int64_t)1 << 31) || (int64_t)d->B * d->T >= ((int64_t)1 << 30))
+    return MSA_ERR_SHAPE;
+  g->B = d->B; g->T = d->T; g->G = d->G; g->K = d->topk; g->N = d->T / 128;
+  g->H = d->H; g->D = d->d; g->DP = d->dp;
+  if (op == MSA_OP_SELECT) {
+    if (d->dp != 32 && d->dp != 64 && d->dp != 128) return MSA_ERR_UNSUPPORTED;
+    g->H = g->G; g->R = 1; g->D = 64;
+  } else {
+    if (d->H < 1 || d->H % d->G != 0) return MSA_ERR_SHAPE;
+    g->R = d->H / d->G;
+    if (!is_pow2_le16(g->R) || (d->d != 64 && d->d != 128)) return MSA_ERR_UNSUPPORTED;
+  }
+  g->scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)g->D);
+  return MSA_OK;
+}
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+InvBufs inv_bufs(const Layout& L, char* ws) {
+  InvBufs ib;
+  ib.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  ib.base = reinterpret_cast<int32_t*>(ws + L.base);
+  ib.len = reinterpret_cast<int32_t*>(ws + L.len);
+  ib.items = reinterpret_cast<int4*>(ws + L.items);
+  ib.item_count = reinterpret_cast<int32_t*>(ws + L.item_count);
+  ib.list = reinterpret_cast<int32_t*>(ws + L.list);
+  ib.max_items = L.max_items;
+  return ib;
+}
+
+#define MSA_TRY(x)                                  \
+  do {                                              \
+    if ((x) != hipSuccess) return MSA_ERR_HIP;      \
+  } while (0)
+
+}  // namespace
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
+  Geo g;
+  if (make_geo(dims, op, &g) != MSA_OK) return 0;
+  const size_t full = layout(g, op, g.T).total;
+  const size_t cap = op == MSA_OP_SELECT ? CAP_SELECT : CAP_MAIN;
+  if (full <= cap) return full;
+  const int W = fit_window(g, op, cap);
+  return layout(g, op, W > 0 ? W : min_window(g)).total;
+}
+
+size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op) {
+  Geo g;
+  if (make_geo(dims, op, &g) != MSA_OK) return 0;
+  return layout(g, op, min_window(g)).total;
+}
+
+msa_status msa_proxy_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp, int32_t* idx, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Geo g;
+  const msa_status s = make_geo(dims, MSA_OP_SELECT, &g);
+  if (s != MSA_OK) return s;
+  if (!qp || !kp || !idx || !ws) return MSA_ERR_NULL;
+  if (!al16(qp) || !al16(kp) || !al16(idx) || !al16(ws)) return MSA_ERR_ALIGN;
+  const int W = fit_window(g, MSA_OP_SELECT, ws_bytes);
+  if (W == 0) return MSA_ERR_WORKSPACE;
+  const Layout L = layout(g, MSA_OP_SELECT, W);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* pooled = reinterpret_cast<float*>(static_cast<char*>(ws) + L.pooled);
+  for (int t0 = 0; t0 < g.T; t0 += W) {
+    const Win w{t0, std::min(W, g.T - t0)};
+    MSA_TRY(launch_proxy_pool(g, w, qp, kp, pooled, st));
+    MSA_TRY(launch_topk(g, w, pooled, idx, st));
+  }
+  return MSA_OK;
+}
+
+msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v, const int32_t* idx,
+                   msa_bf16* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  const msa_status s = make_geo(dims, MSA_OP_FWD, &g);
+  if (s != MSA_OK) return s;
+  if (!q || !k || !v || !idx || !o || !lse || !ws) return MSA_ERR_NULL;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(idx) || !al16(o) || !al16(lse) || !al16(ws)) return MSA_ERR_ALIGN;
+  const int W = fit_window(g, MSA_OP_FWD, ws_bytes);
+  if (W == 0) return MSA_ERR_WORKSPACE;
+  const Layout L = layout(g, MSA_OP_FWD, W);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const InvBufs ib = inv_bufs(L, base);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  for (int t0 = 0; t0 < g.T; t0 += W) {
+    const Win w{t0, std::min(W, g.T - t0)};
+    MSA_TRY(launch_inverse(g, w, idx, ib, FWD_ITEM_TOKENS, st));
+    MSA_TRY(launch_fwd_partials(g, w, q, k, v, ib, part_o, part_lse, st));
+    MSA_TRY(launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, st));
+  }
+  return MSA_OK;
+}
+
+msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v, const msa_bf16* o,
+                   const msa_bf16* dout, const float* lse, const int32_t* idx, msa_bf16* dq, msa_bf16* dk,
+                   msa_bf16* dv, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  const msa_status s = make_geo(dims, MSA_OP_BWD, &g);
+  if (s != MSA_OK) return s;
+  if (!q || !k || !v || !o || !dout || !lse || !idx || !dq || !dk || !dv || !ws) return MSA_ERR_NULL;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al16(dout) || !al16(lse) || !al16(idx) || !al16(dq) ||
+      !al16(dk) || !al16(dv) || !al16(ws))
+    return MSA_ERR_ALIGN;
+  const int W = fit_window(g, MSA_OP_BWD, ws_bytes);
+  if (W == 0) return MSA_ERR_WORKSPACE;
+  const Layout L = layout(g, MSA_OP_BWD, W);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const InvBufs ib = inv_bufs(L, base);
+  float* Dd = reinterpret_cast<float*>(base + L.Dd);
+  float* dk_acc = reinterpret_cast<float*>(base + L.dk_acc);
+  float* dv_acc = reinterpret_cast<float*>(base + L.dv_acc);
+  uint16_t* dq_part = reinterpret_cast<uint16_t*>(base + L.dq_part);
+  const size_t kv = (size_t)g.B * g.T * g.G * g.D;
+  MSA_TRY(launch_bwd_dot(g, o, dout, Dd, st));
+  MSA_TRY(launch_fill_zero(dk_acc, kv, st));
+  MSA_TRY(launch_fill_zero(dv_acc, kv, st));
+  for (int t0 = 0; t0 < g.T; t0 += W) {
+    const Win w{t0, std::min(W, g.T - t0)};
+    MSA_TRY(launch_inverse(g, w, idx, ib, BWD_ITEM_TOKENS, st));
+    MSA_TRY(launch_bwd_partials(g, w, q, k, v, dout, lse, Dd, ib, dq_part, dk_acc, dv_acc, st));
+    MSA_TRY(launch_dq_combine(g, w, idx, dq_part, dq, st));
+  }
+  MSA_TRY(launch_cvt_bf16(dk_acc, dk, kv, st));
+  MSA_TRY(launch_cvt_bf16(dv_acc, dv, kv, st));
+  return MSA_OK;
+}
+
+const char* msa_status_str(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "null pointer argument";
+    case MSA_ERR_SHAPE: return "dimensions out of the supported range";
+    case MSA_ERR_UNSUPPORTED: return "head dim, proxy dim or group ratio not supported";
+    case MSA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* msa_version(void) { return "msa-gfx950 0.1"; }
+
+}  // extern "C"

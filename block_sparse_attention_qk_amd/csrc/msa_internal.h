@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (internal to libmsa).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Geometry shared by every kernel of one call.
+struct Geo {
+  int B, T, H, G, D, DP, K;  // K = topk
+  int R, N;                  // R = H / G, N = T / 128
+  float scale;               // softmax scale
+};
+
+// One window of tokens [t0, t0 + W).
+struct Win {
+  int t0, W;
+};
+
+constexpr int INV_CHUNK = 256;  // tokens per counting-sort chunk
+constexpr int FWD_ITEM_TOKENS = 256;  // tokens per forward work item (list chunk)
+
+// ---- Index Branch
+hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,
+                             float* pooled, hipStream_t st);
+hipError_t launch_topk(const Geo& g, const Win& w, const float* pooled, int32_t* idx, hipStream_t st);
+
+// ---- Inverse (block -> selecting pairs) index for one window
+struct InvBufs {
+  int32_t* counts;      // [BG][nchunk][N]
+  int32_t* base;        // [BG][N]   list start of each block
+  int32_t* len;         // [BG][N]   list length of each block
+  int4* items;          // [BG][max_items]  {block, start, len, 0}
+  int32_t* item_count;  // [BG]
+  int32_t* list;        // [BG][W * K]  pair ids (t - t0) * K + slot
+  int max_items;
+};
+int inv_max_items(const Geo& g, int W, int item_tokens);
+hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const InvBufs& ib,
+                          int item_tokens, hipStream_t st);
+
+// ---- Main Branch
+hipError_t launch_fwd_partials(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const InvBufs& ib, uint16_t* part_o,
+                               float* part_lse, hipStream_t st);
+hipError_t launch_fwd_combine(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* part_o,
+                              const float* part_lse, uint16_t* o, float* lse, hipStream_t st);
+
+hipError_t launch_bwd_dot(const Geo& g, const uint16_t* o, const uint16_t* dout, float* Dd, hipStream_t st);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
+hipError_t launch_bwd_partials(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const uint16_t* dout, const float* lse,
+                               const float* Dd, const InvBufs& ib, uint16_t* dq_part,
+                               float* dk_acc, float* dv_acc, hipStream_t st);
+hipError_t launch_dq_combine(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* dq_part,
+                             uint16_t* dq, hipStream_t st);
+hipError_t launch_cvt_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
+
+}  // namespace msa

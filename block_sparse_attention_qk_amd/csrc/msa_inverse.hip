@@ -1,0 +1,135 @@
+// Inverse of the block-index cache for one window of tokens: for every
+// (batch, group, block) the list of (token, slot) pairs that selected it, plus
+// the work items the KV-stationary Main Branch kernels walk.
+//
+// The cache is the block-index table the Index Branch writes (xcelit page,
+// "How MSA works": everything downstream reads the cached sparse blocks).  Its
+// inverse lets the Main Branch keep one K/V block in LDS and stream the queries
+// that read it.  Built as a counting sort: per-chunk block histograms in LDS,
+// a column scan over chunks, a scan over blocks, then a scatter.
+#include "msa_common.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+// counts[bg][chunk][blk] = number of pairs of the chunk's tokens that picked blk.
+// Entries outside 0..t/128 are ignored.
+__global__ __launch_bounds__(256) void k_inv_count(const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
+                                                   int T, int N, int K, int t0, int W, int nchunk) {
+  extern __shared__ int32_t hist[];
+  const int chunk = blockIdx.x, bg = blockIdx.y;
+  for (int i = threadIdx.x; i < N; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int tl0 = chunk * INV_CHUNK, ntok = min(INV_CHUNK, W - tl0);
+  const int32_t* rows = idx + ((size_t)bg * T + t0 + tl0) * K;
+  for (int e = threadIdx.x; e < ntok * K; e += 256) {
+    const int blk = rows[e];
+    const int t = t0 + tl0 + e / K;
+    if (blk >= 0 && blk <= t / BLK) atomicAdd(&hist[blk], 1);
+  }
+  __syncthreads();
+  int32_t* out = counts + ((size_t)bg * nchunk + chunk) * N;
+  for (int i = threadIdx.x; i < N; i += 256) out[i] = hist[i];
+}
+
+// In place: counts[bg][c][blk] <- sum over chunks before c; len[bg][blk] = total.
+__global__ __launch_bounds__(256) void k_inv_colscan(int32_t* __restrict__ counts, int32_t* __restrict__ len,
+                                                     int N, int nchunk) {
+  const int bg = blockIdx.y, blk = blockIdx.x * 256 + threadIdx.x;
+  if (blk >= N) return;
+  int run = 0;
+  for (int c = 0; c < nchunk; ++c) {
+    const size_t o = ((size_t)bg * nchunk + c) * N + blk;
+    const int v = counts[o];
+    counts[o] = run;
+    run += v;
+  }
+  len[(size_t)bg * N + blk] = run;
+}
+
+// One workgroup per (batch, group): exclusive scan of list lengths -> base,
+// and the work items {block, start, len} that cut each list into pieces of at
+// most item_tokens pairs, in block order.
+__global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restrict__ len, int32_t* __restrict__ base,
+                                                        int4* __restrict__ items, int32_t* __restrict__ item_count,
+                                                        int N, int max_items, int item_tokens) {
+  __shared__ int s_a[1024], s_b[1024];
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  const int per = (N + 1023) / 1024, b0 = tid * per;
+  const int32_t* L = len + (size_t)bg * N;
+  int sl = 0, si = 0;
+  for (int i = 0; i < per; ++i) {
+    const int blk = b0 + i;
+    if (blk < N) {
+      const int l = L[blk];
+      sl += l;
+      si += (l + item_tokens - 1) / item_tokens;
+    }
+  }
+  s_a[tid] = sl;
+  s_b[tid] = si;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = tid >= off ? s_a[tid - off] : 0, b = tid >= off ? s_b[tid - off] : 0;
+    __syncthreads();
+    s_a[tid] += a;
+    s_b[tid] += b;
+    __syncthreads();
+  }
+  int run_l = s_a[tid] - sl, run_i = s_b[tid] - si;
+  if (tid == 1023) item_count[bg] = s_b[1023];
+  int4* it = items + (size_t)bg * max_items;
+  for (int i = 0; i < per; ++i) {
+    const int blk = b0 + i;
+    if (blk >= N) break;
+    const int l = L[blk];
+    base[(size_t)bg * N + blk] = run_l;
+    for (int s = 0; s < l; s += item_tokens) it[run_i++] = make_int4(blk, run_l + s, min(item_tokens, l - s), 0);
+    run_l += l;
+  }
+}
+
+// list[bg][pos] = (t - t0) * K + slot, grouped by block.
+__global__ __launch_bounds__(256) void k_inv_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ base, int32_t* __restrict__ list,
+                                                     int T, int N, int K, int t0, int W, int nchunk) {
+  extern __shared__ int32_t cur[];
+  const int chunk = blockIdx.x, bg = blockIdx.y;
+  const int32_t* cc = counts + ((size_t)bg * nchunk + chunk) * N;
+  const int32_t* bs = base + (size_t)bg * N;
+  for (int i = threadIdx.x; i < N; i += 256) cur[i] = bs[i] + cc[i];
+  __syncthreads();
+  const int tl0 = chunk * INV_CHUNK, ntok = min(INV_CHUNK, W - tl0);
+  const int32_t* rows = idx + ((size_t)bg * T + t0 + tl0) * K;
+  int32_t* out = list + (size_t)bg * W * K;
+  for (int e = threadIdx.x; e < ntok * K; e += 256) {
+    const int blk = rows[e];
+    const int t = t0 + tl0 + e / K;
+    if (blk >= 0 && blk <= t / BLK) {
+      const int pos = atomicAdd(&cur[blk], 1);
+      out[pos] = tl0 * K + e;
+    }
+  }
+}
+
+int inv_max_items(const Geo& g, int W, int item_tokens) {
+  const long long pairs = (long long)W * g.K;
+  long long m = g.N + pairs / item_tokens + 1;
+  if (m > pairs + g.N) m = pairs + g.N;
+  return (int)m;
+}
+
+hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const InvBufs& ib, int item_tokens,
+                          hipStream_t st) {
+  const int BG = g.B * g.G;
+  const int nchunk = (w.W + INV_CHUNK - 1) / INV_CHUNK;
+  const size_t lds = (size_t)g.N * sizeof(int32_t);
+  k_inv_count<<<dim3(nchunk, BG), 256, lds, st>>>(idx, ib.counts, g.T, g.N, g.K, w.t0, w.W, nchunk);
+  k_inv_colscan<<<dim3((g.N + 255) / 256, BG), 256, 0, st>>>(ib.counts, ib.len, g.N, nchunk);
+  k_inv_blockscan<<<BG, 1024, 0, st>>>(ib.len, ib.base, ib.items, ib.item_count, g.N, ib.max_items, item_tokens);
+  k_inv_scatter<<<dim3(nchunk, BG), 256, lds, st>>>(idx, ib.counts, ib.base, ib.list, g.T, g.N, g.K, w.t0, w.W,
+                                                     nchunk);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,136 @@
+/*
+ * msa.h - C ABI of the MI355X (gfx950) MiniMax Sparse Attention training hot path.
+ *
+ * What is computed (sources are the three pages on Flash-MSA / MiniMax Sparse
+ * Attention; the method is described in prose only):
+ *
+ *   Index Branch  - msa_proxy_select
+ *     One proxy head per GQA group scores each query against every causal key,
+ *     the scores are max-pooled over 128-key blocks, and the top-k blocks of
+ *     each query are kept as that query's block-index cache.
+ *     ("Flash-MSA: Open-Source Sparse Attention Kernels Debut", section "How MSA
+ *     works": 128-key blocks picked by max-pooling proxy scores, indices cached
+ *     so only the proxy pass stays quadratic, group-wise proxy heads;
+ *     ai-beat "flash-msa-sparse-attention-training", paragraphs 1, 3 and 4.)
+ *
+ *   Main Branch   - msa_fwd, msa_bwd
+ *     Exact softmax GQA attention over only the keys of the cached blocks, and
+ *     its gradients dQ, dK, dV.  (ai-beat page, paragraph 1: exact softmax over
+ *     the selected blocks; paragraph 2: a backward pass through the learned
+ *     sparse pattern; xcelit page, "How MSA works": GQA main attention.)
+ *
+ * Readings where the pages are silent (also listed with the design notes):
+ *   - proxy score = plain dot product q_p . k_p (no scale, no activation);
+ *   - query head h belongs to KV/proxy group g = h / (H / G);
+ *   - query t may pick blocks 0 .. t/128; inside a block only keys j <= t count,
+ *     for pooling and for attention; the diagonal block is an ordinary candidate;
+ *   - equal pooled scores rank the lower block index first; -0 equals +0;
+ *   - a cache row lists its min(topk, t/128 + 1) blocks in ascending order and
+ *     is padded with -1;
+ *   - softmax scale = dims.scale, or 1/sqrt(d) when dims.scale <= 0;
+ *   - lse is the natural-log log-sum-exp of the scaled scores.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers owned by the caller, row-major,
+ *     contiguous, 16-byte aligned.  bf16 values are passed as raw 16-bit words.
+ *       qp, kp            [B, T, G, dp]  bf16
+ *       q, o, dout, dq    [B, T, H, d]   bf16
+ *       k, v, dk, dv      [B, T, G, d]   bf16
+ *       idx               [B, G, T, topk] int32 (the block-index cache)
+ *       lse               [B, T, H]      fp32
+ *   - ws / ws_bytes is caller-owned device scratch memory.  msa_workspace_bytes
+ *     gives the size that lets a call run in one pass over the tokens; any size
+ *     at or above msa_workspace_min_bytes works (smaller sizes make the call
+ *     walk the tokens in more windows).  Its contents need no initialisation
+ *     and are undefined afterwards.  The library allocates no device memory.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; outputs are valid once the stream
+ *     reaches that point.  Calls on one workspace must not overlap.
+ *   - Argument checks happen on the host before anything is enqueued; a
+ *     failing check returns an error code and enqueues nothing.  A launch
+ *     failure returns MSA_ERR_HIP.  Outputs are fully overwritten.
+ *   - Supported shapes: B >= 1; T >= 128 with T % 128 == 0; H % G == 0 with
+ *     R = H / G in {1, 2, 4, 8, 16}; d in {64, 128}; dp in {32, 64, 128};
+ *     1 <= topk <= 1024 (topk may exceed the number of causal blocks);
+ *     T * topk < 2^31.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t msa_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MSA_ERR_SHAPE = 2,       /* dims out of the supported range */
+  MSA_ERR_UNSUPPORTED = 3, /* a head dim / proxy dim / group ratio not built */
+  MSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  MSA_ERR_WORKSPACE = 5,   /* ws_bytes below msa_workspace_min_bytes */
+  MSA_ERR_HIP = 6          /* the HIP runtime reported an error */
+} msa_status;
+
+typedef struct {
+  int32_t B, T, H, G, d, dp, topk;
+  float scale; /* softmax scale; <= 0 selects 1/sqrt(d) */
+} msa_dims;
+
+typedef enum { MSA_OP_SELECT = 0, MSA_OP_FWD = 1, MSA_OP_BWD = 2 } msa_op;
+
+/* Workspace that lets `op` process all tokens in one window (capped at a
+ * few tens of GiB for the largest shapes, which are then walked in windows).
+ * Returns 0 for invalid dims. */
+size_t msa_workspace_bytes(const msa_dims* dims, msa_op op);
+
+/* Smallest workspace `op` accepts (one 128-token window).  0 for invalid dims. */
+size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op);
+
+/* Index Branch.  For every (b, g, t): pooled_i = max over keys j of block i
+ * with j <= t of dot(qp[b,t,g,:], kp[b,j,g,:]) (fp32), for i <= t/128; the
+ * min(topk, t/128+1) highest pooled blocks (ties: lower index) are written
+ * ascending to idx[b,g,t,:], the rest of the row is -1.  Reads qp and kp;
+ * writes idx. */
+msa_status msa_proxy_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Main Branch forward.  For every (b, t, h), g = h / (H/G), over the key set
+ * J = { j <= t : j/128 is listed in idx[b,g,t,:] } and s_j = scale * q.k_j:
+ *   o[b,t,h,:] = sum_j softmax(s)_j v[b,j,g,:]   (bf16, round to nearest even)
+ *   lse[b,t,h] = max_j s_j + ln sum_j exp(s_j - max_j s_j)            (fp32)
+ * idx must be a valid cache (entries in 0..t/128 or -1, no repeats, at least
+ * one entry per row): rows produced by msa_proxy_select always are. */
+msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                   const int32_t* idx, msa_bf16* o, float* lse, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Main Branch backward of L = sum(o * dout) through the same sparse pattern,
+ * with P_j = exp(s_j - lse), D = dot(dout, o) (o as stored in bf16),
+ * dS_j = P_j (dot(dout, v_j) - D):
+ *   dq[b,t,h,:] = scale * sum_j dS_j k_j
+ *   dk[b,j,g,:] = scale * sum_{t,h in g} dS_{t,h,j} q[b,t,h,:]
+ *   dv[b,j,g,:] =         sum_{t,h in g} P_{t,h,j} dout[b,t,h,:]
+ * (keys no query reads get zero gradients).  o and lse are msa_fwd's outputs
+ * for the same q, k, v, idx.  No gradient flows to qp/kp: the top-k choice is
+ * piecewise constant. */
+msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                   const msa_bf16* o, const msa_bf16* dout, const float* lse, const int32_t* idx,
+                   msa_bf16* dq, msa_bf16* dk, msa_bf16* dv, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* msa_status_str(msa_status s);
+
+/* Library version string, e.g. "msa-gfx950 0.1". */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */
