@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA training hot path on one MI355X (gfx950).
+
+One step is the whole hot path over one batch of synthetic input:
+msa_proxy_select (Index Branch: proxy score, block max-pool, top-k into the
+block-index cache) -> msa_fwd -> msa_bwd (Main Branch over the cached blocks).
+Inputs are resident in HBM before the timed region.  W warm-up steps, then K
+timed steps between two device synchronisations.
+
+Printed: one JSON line.  `value` is tokens/s of the whole step on the main
+workload (the 128K configuration: B=1, T=131072, 32 query / 4 KV heads, head
+dim 128, 4 proxy heads of dim 64, top-k 32).  Extra fields give the fwd+bwd
+rate with cached indices, effective TFLOP/s on the executed sparse FLOPs,
+per-phase and per-kernel times (HIP events recorded by the library on the
+launch stream), the roofline of the dominant kernel, the 1M configuration as
+a second workload, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m|''] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import block_sparse_attention_qk_amd as msa  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+METRIC = "MSA fwd+bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), 128K & 1M"
+
+
+def gpu_inputs(cfg: synth.Config, seed: int = 0) -> dict:
+    """Same recipe as synth (N(0,1) bf16; proxy keys plus a per-block mean of
+    variance 0.5) drawn directly on the GPU, for workloads too large to draw
+    on the host in reasonable time.  Values differ from synth's CPU draws."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    out = {}
+    shapes = {"q": (cfg.B, cfg.T, cfg.H, cfg.d), "dout": (cfg.B, cfg.T, cfg.H, cfg.d),
+              "k": (cfg.B, cfg.T, cfg.G, cfg.d), "v": (cfg.B, cfg.T, cfg.G, cfg.d),
+              "qp": (cfg.B, cfg.T, cfg.G, cfg.dp), "kp": (cfg.B, cfg.T, cfg.G, cfg.dp)}
+    for i, (name, shp) in enumerate(shapes.items()):
+        g.manual_seed(0x5EED + 7919 * (i + 1) + seed)
+        t = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+        flat = t.view(-1)
+        step = 1 << 26
+        for s in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - s)
+            flat[s:s + n] = torch.randn(n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        out[name] = t
+    g.manual_seed(0x5EED + 7919 * 7 + seed)
+    mu = torch.randn((cfg.B, cfg.N, cfg.G, cfg.dp), generator=g, device=dev) * math.sqrt(0.5)
+    kp = out["kp"].float().view(cfg.B, cfg.N, synth.BLOCK, cfg.G, cfg.dp) + mu[:, :, None]
+    out["kp"] = kp.view(cfg.B, cfg.T, cfg.G, cfg.dp).to(torch.bfloat16).contiguous()
+    del kp, mu
+    return out
+
+
+def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool) -> dict:
+    if host_inputs:
+        x = {n: t.cuda() for n, t in synth.make_inputs(cfg).items()}
+    else:
+        x = gpu_inputs(cfg)
+    dims = (cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    ws_bytes = max(msa.msa_workspace_bytes(*dims, op) for op in (msa.OP_SELECT, msa.OP_FWD, msa.OP_BWD))
+    ws = msa.Workspace(nbytes=ws_bytes)
+    idx = torch.empty((cfg.B, cfg.G, cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        msa.msa_proxy_select(x["qp"], x["kp"], cfg.topk, ws=ws, out=idx)
+        if ev:
+            ev[1].record()
+        msa.msa_fwd(x["q"], x["k"], x["v"], idx, ws=ws, out=(o, lse))
+        if ev:
+            ev[2].record()
+        msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, ws=ws, out=(dq, dk, dv))
+        if ev:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    msa.timing_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    phase = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(3)]
+    kern = msa.timing_read()
+    msa.timing_enable(False)
+
+    tokens = cfg.B * cfg.T
+    ms_step = total_ms / steps
+    t_sel, t_fwd, t_bwd = (p / steps for p in phase)
+    f_fwd, f_bwd, f_proxy = cfg.flops_fwd(), cfg.flops_bwd(), cfg.flops_proxy()
+    pairs = cfg.pairs()
+    res = {
+        "workload": cfg.name,
+        "shape": {"B": cfg.B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk},
+        "ms_per_step": ms_step,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "tokens_per_s": tokens / (ms_step / 1e3),
+        "phases_ms": {"select": t_sel, "fwd": t_fwd, "bwd": t_bwd},
+        "fwd_bwd_tokens_per_s": tokens / ((t_fwd + t_bwd) / 1e3),
+        "fwd_bwd_effective_tflops": (f_fwd + f_bwd) / ((t_fwd + t_bwd) / 1e3) / 1e12,
+        "select_tflops": f_proxy / (t_sel / 1e3) / 1e12,
+        "pairs": pairs,
+        "flops": {"fwd": f_fwd, "bwd": f_bwd, "proxy": f_proxy},
+        "kernels_ms_per_step": {k: v[0] / steps for k, v in kern.items()},
+        "kernel_launches_per_step": {k: v[1] / steps for k, v in kern.items()},
+    }
+    res["fwd_bwd_frac_of_peak"] = res["fwd_bwd_effective_tflops"] / PEAK_BF16_TFLOPS
+    res["roofline"] = roofline(cfg, kern, steps)
+    del x, ws, idx, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline(cfg: synth.Config, kern: dict, steps: int) -> dict:
+    """Roofline entry of the kernel with the largest time: algorithmic work per
+    launch divided by its average launch duration."""
+    name = max(kern, key=lambda k: kern[k][0])
+    ms, launches = kern[name]
+    avg_s = ms / max(launches, 1) / 1e3
+    per_step_launch = launches / steps
+    BG = cfg.B * cfg.G
+    if name == "bwd_partials":
+        work, bound, unit = cfg.flops_bwd() / per_step_launch, "mfma", "TFLOP/s"
+    elif name == "fwd_partials":
+        work, bound, unit = cfg.flops_fwd() / per_step_launch, "mfma", "TFLOP/s"
+    elif name == "proxy_pool":
+        work, bound, unit = cfg.flops_proxy() / per_step_launch, "mfma", "TFLOP/s"
+    elif name in ("fwd_combine", "dq_combine"):
+        # read every partial (bf16) once, write the bf16 result (+ lse for fwd)
+        work = (cfg.pairs() * cfg.R * cfg.d * 2 + cfg.B * cfg.T * cfg.H * cfg.d * 2) / per_step_launch
+        bound, unit = "hbm", "GB/s"
+    else:
+        work = float("nan")
+        bound, unit = "hbm", "GB/s"
+    if unit == "TFLOP/s":
+        achieved, peak = work / avg_s / 1e12, PEAK_BF16_TFLOPS
+    else:
+        achieved, peak = work / avg_s / 1e9, PEAK_HBM_GBS
+    return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": None, "avg_launch_ms": avg_s * 1e3,
+            "work_per_launch": work}
+
+
+def cpu_baseline(cfg: synth.Config, target_s: float = 15.0) -> dict:
+    """The oracle, as it stands, on a uniform sample of query tokens of the same
+    workload: Index Branch rows, forward rows and backward dQ rows."""
+    import numpy as np
+    import oracle
+
+    oracle.build()
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    x = synth.make_inputs(cfg)
+    f64 = {n: x[n].double().numpy() for n in x}
+    dm = oracle.Dims(cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    rng = np.random.default_rng(1)
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(cfg.B * cfg.T, size=n_rows, replace=False))
+        t0 = time.perf_counter()
+        sel = oracle.select(dm, f64["qp"], f64["kp"], rows=rows)                 # [n, G, k]
+        idx = np.full((cfg.B, cfg.G, cfg.T, cfg.topk), -1, dtype=np.int32)
+        b_, t_ = rows // cfg.T, rows % cfg.T
+        idx[b_, :, t_, :] = sel
+        oracle.fwd(dm, f64["q"], f64["k"], f64["v"], idx, rows=rows)
+        oracle.bwd_rows(dm, f64["q"], f64["k"], f64["v"], f64["dout"], idx, rows=rows)
+        return time.perf_counter() - t0
+
+    pilot_rows = 16
+    t_pilot = run(pilot_rows)
+    n = int(min(4096, max(pilot_rows, pilot_rows * target_s / max(t_pilot, 1e-3))))
+    t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": ("%d query tokens drawn uniformly from the %s workload: Index Branch rows, forward rows and "
+                       "backward dQ rows over all heads and groups (the oracle's dK/dV pass is not in the sample); "
+                       "%.1f s on %d threads" % (n, cfg.name, t, cores))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--also", default="1m", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--also-steps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    msa.load()
+    cfg = synth.CONFIGS[args.config]
+    print("bench: %s steps=%d warmup=%d" % (cfg, args.steps, args.warmup), file=sys.stderr, flush=True)
+    main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=True)
+    print("bench: main workload done: %.3f ms/step" % main_res["ms_per_step"], file=sys.stderr, flush=True)
+    extra = []
+    for name in [s for s in args.also.split(",") if s and s != args.config]:
+        c = synth.CONFIGS[name]
+        print("bench: extra workload %s" % (c,), file=sys.stderr, flush=True)
+        extra.append(run_workload(c, args.also_steps, 1, host_inputs=False))
+        print("bench: %s done: %.1f ms/step" % (name, extra[-1]["ms_per_step"]), file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg)
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d T=%d H=%d G=%d d=%d dp=%d topk=%d; step = proxy select + fwd + bwd" % (
+            cfg.name, cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk),
+            "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "none (1 GPU)"},
+        "roofline": {k: main_res["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_kernel": main_res["roofline"]["kernel"],
+        "cpu_baseline": cpu,
+        "fwd_bwd_tokens_per_s": main_res["fwd_bwd_tokens_per_s"],
+        "fwd_bwd_effective_tflops": main_res["fwd_bwd_effective_tflops"],
+        "fwd_bwd_frac_of_bf16_peak": main_res["fwd_bwd_frac_of_peak"],
+        "phases_ms": main_res["phases_ms"],
+        "kernels_ms_per_step": main_res["kernels_ms_per_step"],
+        "workloads": [main_res] + extra,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -26,6 +26,7 @@ import torch
 __all__ = [
     "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
     "msa_proxy_select", "msa_fwd", "msa_bwd", "OP_SELECT", "OP_FWD", "OP_BWD", "EXPORTED_SYMBOLS",
+    "KERNEL_NAMES", "timing_enable", "timing_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,11 @@ _lib = None
 
 OP_SELECT, OP_FWD, OP_BWD = 0, 1, 2
 EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_fwd",
-                    "msa_bwd", "msa_status_str", "msa_version")
+                    "msa_bwd", "msa_status_str", "msa_version", "msa_timing_enable", "msa_timing_read")
+
+# msa_kernel_id values (include/msa.h)
+KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
+                "dq_combine", "convert")
 
 
 class MsaError(RuntimeError):
@@ -72,6 +77,10 @@ def load():
     lib.msa_status_str.argtypes = [I]
     lib.msa_status_str.restype = ctypes.c_char_p
     lib.msa_version.restype = ctypes.c_char_p
+    lib.msa_timing_enable.argtypes = [I]
+    lib.msa_timing_enable.restype = None
+    lib.msa_timing_read.argtypes = [P, P, ctypes.c_int32]
+    lib.msa_timing_read.restype = I
     _lib = lib
     return lib
 
@@ -91,6 +100,20 @@ def msa_workspace_bytes(B, T, H, G, d, dp, topk, op, scale: float = 0.0) -> int:
 
 def msa_workspace_min_bytes(B, T, H, G, d, dp, topk, op, scale: float = 0.0) -> int:
     return int(load().msa_workspace_min_bytes(ctypes.byref(_dims(B, T, H, G, d, dp, topk, scale)), op))
+
+
+def timing_enable(on: bool = True) -> None:
+    """Turn the library's per-launch HIP-event timing on or off (clears it)."""
+    load().msa_timing_enable(1 if on else 0)
+
+
+def timing_read() -> dict:
+    """{kernel name: (total ms, launches)} for launches timed since timing_enable."""
+    n = len(KERNEL_NAMES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(load().msa_timing_read(ms, cnt, n))
+    return {KERNEL_NAMES[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
 
 
 class Workspace:

@@ -130,6 +130,42 @@ InvBufs inv_bufs(const Layout& L, char* ws) {
     if ((x) != hipSuccess) return MSA_ERR_HIP;      \
   } while (0)
 
+// ---- opt-in launch timing (process-wide; see msa_timing_enable)
+constexpr int MAX_TIMED = 4096;
+struct TimedLaunch {
+  hipEvent_t a = nullptr, b = nullptr;
+  int kernel = 0;
+};
+struct TimingState {
+  bool on = false;
+  int n = 0;
+  TimedLaunch slot[MAX_TIMED];
+};
+TimingState g_timing;
+
+int timing_begin(int kernel, hipStream_t st) {
+  if (!g_timing.on || g_timing.n >= MAX_TIMED) return -1;
+  TimedLaunch& s = g_timing.slot[g_timing.n];
+  if (!s.a && hipEventCreate(&s.a) != hipSuccess) return -1;
+  if (!s.b && hipEventCreate(&s.b) != hipSuccess) return -1;
+  if (hipEventRecord(s.a, st) != hipSuccess) return -1;
+  s.kernel = kernel;
+  return g_timing.n++;
+}
+
+void timing_end(int id, hipStream_t st) {
+  if (id >= 0) (void)hipEventRecord(g_timing.slot[id].b, st);
+}
+
+// Launch `call` (a hipError_t expression), timed as `kernel` when timing is on.
+#define MSA_LAUNCH(kernel, st, call)                 \
+  do {                                               \
+    const int tid_ = timing_begin((kernel), (st));   \
+    const hipError_t e_ = (call);                    \
+    timing_end(tid_, (st));                          \
+    if (e_ != hipSuccess) return MSA_ERR_HIP;        \
+  } while (0)
+
 }  // namespace
 }  // namespace msa
 
@@ -167,8 +203,8 @@ msa_status msa_proxy_select(const msa_dims* dims, const msa_bf16* qp, const msa_
   float* pooled = reinterpret_cast<float*>(static_cast<char*>(ws) + L.pooled);
   for (int t0 = 0; t0 < g.T; t0 += W) {
     const Win w{t0, std::min(W, g.T - t0)};
-    MSA_TRY(launch_proxy_pool(g, w, qp, kp, pooled, st));
-    MSA_TRY(launch_topk(g, w, pooled, idx, st));
+    MSA_LAUNCH(MSA_K_PROXY_POOL, st, launch_proxy_pool(g, w, qp, kp, pooled, st));
+    MSA_LAUNCH(MSA_K_TOPK, st, launch_topk(g, w, pooled, idx, st));
   }
   return MSA_OK;
 }
@@ -190,9 +226,9 @@ msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
   for (int t0 = 0; t0 < g.T; t0 += W) {
     const Win w{t0, std::min(W, g.T - t0)};
-    MSA_TRY(launch_inverse(g, w, idx, ib, FWD_ITEM_TOKENS, st));
-    MSA_TRY(launch_fwd_partials(g, w, q, k, v, ib, part_o, part_lse, st));
-    MSA_TRY(launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, st));
+    MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse(g, w, idx, ib, FWD_ITEM_TOKENS, st));
+    MSA_LAUNCH(MSA_K_FWD_PARTIALS, st, launch_fwd_partials(g, w, q, k, v, ib, part_o, part_lse, st));
+    MSA_LAUNCH(MSA_K_FWD_COMBINE, st, launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, st));
   }
   return MSA_OK;
 }
@@ -218,17 +254,17 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   float* dv_acc = reinterpret_cast<float*>(base + L.dv_acc);
   uint16_t* dq_part = reinterpret_cast<uint16_t*>(base + L.dq_part);
   const size_t kv = (size_t)g.B * g.T * g.G * g.D;
-  MSA_TRY(launch_bwd_dot(g, o, dout, Dd, st));
-  MSA_TRY(launch_fill_zero(dk_acc, kv, st));
-  MSA_TRY(launch_fill_zero(dv_acc, kv, st));
+  MSA_LAUNCH(MSA_K_BWD_DOT, st, launch_bwd_dot(g, o, dout, Dd, st));
+  MSA_LAUNCH(MSA_K_BWD_DOT, st, launch_fill_zero(dk_acc, kv, st));
+  MSA_LAUNCH(MSA_K_BWD_DOT, st, launch_fill_zero(dv_acc, kv, st));
   for (int t0 = 0; t0 < g.T; t0 += W) {
     const Win w{t0, std::min(W, g.T - t0)};
-    MSA_TRY(launch_inverse(g, w, idx, ib, BWD_ITEM_TOKENS, st));
-    MSA_TRY(launch_bwd_partials(g, w, q, k, v, dout, lse, Dd, ib, dq_part, dk_acc, dv_acc, st));
-    MSA_TRY(launch_dq_combine(g, w, idx, dq_part, dq, st));
+    MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse(g, w, idx, ib, BWD_ITEM_TOKENS, st));
+    MSA_LAUNCH(MSA_K_BWD_PARTIALS, st, launch_bwd_partials(g, w, q, k, v, dout, lse, Dd, ib, dq_part, dk_acc, dv_acc, st));
+    MSA_LAUNCH(MSA_K_DQ_COMBINE, st, launch_dq_combine(g, w, idx, dq_part, dq, st));
   }
-  MSA_TRY(launch_cvt_bf16(dk_acc, dk, kv, st));
-  MSA_TRY(launch_cvt_bf16(dv_acc, dv, kv, st));
+  MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dk_acc, dk, kv, st));
+  MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dv_acc, dv, kv, st));
   return MSA_OK;
 }
 
@@ -246,5 +282,28 @@ const char* msa_status_str(msa_status s) {
 }
 
 const char* msa_version(void) { return "msa-gfx950 0.1"; }
+
+void msa_timing_enable(int on) {
+  g_timing.on = on != 0;
+  g_timing.n = 0;
+}
+
+msa_status msa_timing_read(double* ms, int32_t* launches, int32_t n) {
+  for (int k = 0; k < n; ++k) {
+    if (ms) ms[k] = 0.0;
+    if (launches) launches[k] = 0;
+  }
+  for (int i = 0; i < g_timing.n; ++i) {
+    const TimedLaunch& s = g_timing.slot[i];
+    float t = 0.f;
+    if (hipEventSynchronize(s.b) != hipSuccess || hipEventElapsedTime(&t, s.a, s.b) != hipSuccess)
+      return MSA_ERR_HIP;
+    if (s.kernel < n) {
+      if (ms) ms[s.kernel] += t;
+      if (launches) launches[s.kernel] += 1;
+    }
+  }
+  return MSA_OK;
+}
 
 }  // extern "C"

@@ -123,6 +123,36 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
                    msa_bf16* dq, msa_bf16* dk, msa_bf16* dv, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* ---- Optional launch timing, for benchmarks and profiling tools.
+ * When enabled, the library records a pair of HIP events on the call's stream
+ * around every launch of the kernels listed below (the inverse-index build
+ * counts as one launch of four kernels).  Timing state is process-wide and
+ * not thread-safe; it is off by default and costs nothing when off.  At most
+ * 4096 launches are recorded between two msa_timing_enable calls; later
+ * launches run untimed.  Events are created on first use and kept until the
+ * process ends. */
+typedef enum {
+  MSA_K_PROXY_POOL = 0,   /* proxy score + block max-pool */
+  MSA_K_TOPK = 1,         /* per-row top-k -> idx */
+  MSA_K_INVERSE = 2,      /* block -> pair inverse index (4 kernels) */
+  MSA_K_FWD_PARTIALS = 3, /* forward per-pair partials (KV-stationary) */
+  MSA_K_FWD_COMBINE = 4,  /* forward log-sum-exp combine */
+  MSA_K_BWD_DOT = 5,      /* D = rowsum(dout * o) and accumulator clears */
+  MSA_K_BWD_PARTIALS = 6, /* backward dK/dV + per-pair dQ partials (KV-stationary) */
+  MSA_K_DQ_COMBINE = 7,   /* dQ partial sums */
+  MSA_K_CONVERT = 8,      /* fp32 -> bf16 of dK, dV */
+  MSA_K_COUNT = 9
+} msa_kernel_id;
+
+/* on != 0 enables timing; any call clears what was recorded. */
+void msa_timing_enable(int on);
+
+/* Waits for the recorded events and writes, for each msa_kernel_id k < n,
+ * the summed duration in milliseconds to ms[k] and the number of timed
+ * launches to launches[k] (either array may be NULL).  Returns MSA_OK, or
+ * MSA_ERR_HIP if an event could not be read. */
+msa_status msa_timing_read(double* ms, int32_t* launches, int32_t n);
+
 /* Static description of a status code (never NULL). */
 const char* msa_status_str(msa_status s);
 
