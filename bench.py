@@ -212,6 +212,8 @@ def main() -> int:
     ap.add_argument("--also", default="1m", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gpu-inputs", action="store_true",
+                    help="draw the main workload's inputs on the GPU (same recipe, different stream; for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
@@ -223,7 +225,7 @@ def main() -> int:
     msa.load()
     cfg = synth.CONFIGS[args.config]
     print("bench: %s steps=%d warmup=%d" % (cfg, args.steps, args.warmup), file=sys.stderr, flush=True)
-    main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=True)
+    main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=not args.gpu_inputs)
     print("bench: main workload done: %.3f ms/step" % main_res["ms_per_step"], file=sys.stderr, flush=True)
     extra = []
     for name in [s for s in args.also.split(",") if s and s != args.config]:

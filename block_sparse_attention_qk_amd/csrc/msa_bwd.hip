@@ -5,14 +5,17 @@
 //
 // KV-stationary schedule, one work item per (batch, group, block) and window.
 // Each of the 4 waves owns 32 keys of the block: their K and V rows stay in
-// registers as MFMA operands, their dK/dV accumulate in registers over all
-// the pairs that read the block.  Tiles of 64 query rows (64/R tokens x R
-// heads) are staged in LDS in row-major and transposed form.  Per tile:
+// registers as MFMA operands and their dK/dV accumulate in registers over all
+// pairs that read the block.  Tiles of 64 query rows (64/R tokens x R heads)
+// stream through a double-buffered LDS tile in plain row-major form; the
+// global loads of tile i+2 are in flight while tile i computes.  Per tile
+// (v_mfma_f32_32x32x16_bf16 throughout):
 //   S = Q K^T, dP = dO V^T           (rows along M, owned keys along N)
 //   P = exp(scale S - LSE), dS = P (dP - D)
-//   dV += P^T dO, dK += dS^T Q        (P, dS reused in place as A operands)
-//   dQ^T = K^T dS^T                   (dS exchanged through LDS; each wave
-//                                      makes a 16- or 32-wide slice of dQ)
+//   dV += P^T dO, dK += dS^T Q        (P, dS reused in place as A operands;
+//                                      dO, Q read with LDS transpose reads)
+//   dQ^T = K^T dS^T                   (dS^T exchanged through LDS; each wave
+//                                      makes one 32-wide slice of dQ)
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
 // token's partials.  dK/dV are added into fp32 accumulators once per item.
 // Nothing is accumulated with atomics.
@@ -23,6 +26,14 @@
 
 namespace msa {
 
+// Position of 16-byte chunk c of row r in a swizzled row-major tile of
+// DCH chunks per row: consecutive rows land on distinct LDS banks both for
+// 16-byte row reads and for transpose reads of 4 rows x 32 bytes.
+template <int DCH>
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (DCH - 1));
+}
+
 template <int D, int R>
 __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     const bf16raw* __restrict__ q, const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
@@ -30,217 +41,217 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     const int4* __restrict__ items, const int32_t* __restrict__ item_count, const int32_t* __restrict__ list,
     bf16raw* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc, int T, int H, int G,
     int K, int t0, int W, int max_items, float scale, float sl2) {
-  constexpr int KS = D / 32;     // k-steps over the head dim
-  constexpr int CT = D / 16;     // head-dim tiles
-  constexpr int CW = D / 64;     // head-dim tiles of dQ made by each wave
+  constexpr int KSD = D / 16;    // 32x32x16 k-steps over the head dim
+  constexpr int NCT = D / 32;    // 32-wide head-dim tiles
+  constexpr int DCH = D / 8;     // 16-byte chunks per row
   constexpr int TR = 64;         // query rows per tile
   constexpr int TT = TR / R;     // tokens per tile
-  constexpr int LDQ = D + 8;     // row-major tile stride (bf16)
-  constexpr int LDT = TR + 8;    // transposed tile stride (bf16)
-  constexpr int LDS_ = BLK + 8;  // dS tile stride (bf16)
-  __shared__ __attribute__((aligned(16))) bf16raw Qs[TR * LDQ];
-  __shared__ __attribute__((aligned(16))) bf16raw dOs[TR * LDQ];
-  __shared__ __attribute__((aligned(16))) bf16raw QsT[D * LDT];
-  __shared__ __attribute__((aligned(16))) bf16raw dOsT[D * LDT];
-  __shared__ __attribute__((aligned(16))) bf16raw dSs[TR * LDS_];
-  __shared__ float lse_s[TR], dd_s[TR];
-  __shared__ int tok_s[TR], pair_s[TR];
+  constexpr int CPT = DCH / 4;   // chunks per thread per staged matrix (thread = one row)
+  constexpr int LDT = TR + 8;    // dS^T row stride (bf16)
+  // dQ^T work split: (head-dim tile, row tile) pairs spread over the 4 waves
+  constexpr int QCT = NCT == 4 ? 1 : 1;            // head-dim tiles per wave
+  constexpr int QNT = NCT == 4 ? 2 : 1;            // row tiles per wave
+  __shared__ __attribute__((aligned(16))) bf16raw Qs[2][TR * D];
+  __shared__ __attribute__((aligned(16))) bf16raw dOs[2][TR * D];
+  __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
+  __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
+  __shared__ __attribute__((aligned(16))) bf16raw dSt[BLK * LDT];
+  __shared__ __attribute__((aligned(16))) float rlse[2][TR];
+  __shared__ __attribute__((aligned(16))) float rdd[2][TR];
+  __shared__ __attribute__((aligned(16))) int rlim[2][TR];
+  __shared__ __attribute__((aligned(16))) int rpair[2][TR];
 
   const int bg = blockIdx.y;
   if ((int)blockIdx.x >= item_count[bg]) return;
   const int4 it = items[(size_t)bg * max_items + blockIdx.x];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
   const size_t kv0 = (size_t)(b * T + blk * BLK) * G + g;
   const size_t pair0 = (size_t)bg * W * K;
   const int32_t* lst = list + pair0 + start;
-  const int kw = 32 * wave;            // first key owned by this wave
-  const int cbase = 16 * CW * wave;    // first dQ column made by this wave
-
-  bf16x8 bk[2][KS], bv[2][KS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const size_t rrow = (kv0 + (size_t)(kw + 16 * nt + l16) * G) * D + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bk[nt][ks] = ld8(k + rrow + 32 * ks);
-      bv[nt][ks] = ld8(v + rrow + 32 * ks);
-    }
-  }
-  // K^T slice (head-dim rows cbase.., all 128 keys in kperm slot order)
-  bf16x8 akt[CW][4];
-#pragma unroll
-  for (int cw = 0; cw < CW; ++cw)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint32_t w[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // slots e = 2m, 2m+1 hold keys of the kperm order (see msa_common.h)
-        const int e0 = 2 * m, e1 = 2 * m + 1;
-        const int k0 = 32 * ks + (e0 < 4 ? 4 * q4 + e0 : 16 + 4 * q4 + (e0 - 4));
-        const int k1 = 32 * ks + (e1 < 4 ? 4 * q4 + e1 : 16 + 4 * q4 + (e1 - 4));
-        const uint32_t lo = k[(kv0 + (size_t)k0 * G) * D + cbase + 16 * cw + l16];
-        const uint32_t hi = k[(kv0 + (size_t)k1 * G) * D + cbase + 16 * cw + l16];
-        w[m] = lo | (hi << 16);
-      }
-      akt[cw][ks] = as_bf8(make_uint4(w[0], w[1], w[2], w[3]));
-    }
-
-  f32x4 dka[2][CT], dva[2][CT];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) dka[nt][ct] = dva[nt][ct] = zero4();
-
+  const int kw = 32 * wave;  // first key owned by this wave
   const int ntiles = (len + TT - 1) / TT;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    // ---- stage rows: Q, dO (row-major and transposed), LSE, D
-    if (threadIdx.x < TR) {
-      const int row = threadIdx.x, li = tile * TT + row / R;
-      const bool val = li < len;
-      const int p = val ? lst[li] : -1;
-      const int t = val ? t0 + p / K : -1;
-      const size_t hrow = (size_t)(b * T + (val ? t : 0)) * H + g * R + row % R;
-      tok_s[row] = t;
-      pair_s[row] = p;
-      lse_s[row] = val ? lse[hrow] * LOG2E : INFINITY;
-      dd_s[row] = val ? Dd[hrow] : 0.f;
+
+  // ---- K and V blocks -> LDS (swizzled row-major)
+  for (int c = tid; c < BLK * DCH; c += 256) {
+    const int r = c / DCH, cc = c % DCH;
+    const size_t src = (kv0 + (size_t)r * G) * D + 8 * cc;
+    st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], ld16u(k + src));
+    st16u(&Vs[r * D + 8 * swz<DCH>(r, cc)], ld16u(v + src));
+  }
+  f32x16 dka[NCT], dva[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dka[ct] = dva[ct] = zero16();
+
+  // ---- staging of one tile: thread tid owns row tid/4 and chunks (tid%4) + 4u
+  const int srow = tid >> 2, ssub = tid & 3;
+  uint4 sq[CPT], sdo[CPT];
+  int s_pair = -1, s_lim = -1;
+  float s_lse = INFINITY, s_dd = 0.f;
+  auto stage_load = [&](int ti) {
+    const int li = ti * TT + srow / R;
+    const bool val = li < len;
+    s_pair = val ? lst[li] : -1;
+    const int t = val ? t0 + s_pair / K : 0;
+    const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      sq[u] = val ? ld16u(q + hrow * D + 8 * (ssub + 4 * u)) : z;
+      sdo[u] = val ? ld16u(dout + hrow * D + 8 * (ssub + 4 * u)) : z;
     }
-    for (int u = threadIdx.x; u < (TR / 2) * (D / 8); u += 256) {
-      const int rp = u & 31, cc = u >> 5;
-      const int r0 = 2 * rp, r1 = r0 + 1;
-      const int li0 = tile * TT + r0 / R, li1 = tile * TT + r1 / R;
-      const bool v0 = li0 < len, v1 = li1 < len;
-      const int t0r = v0 ? t0 + lst[li0] / K : 0, t1r = v1 ? t0 + lst[li1] / K : 0;
-      const size_t a0 = ((size_t)(b * T + t0r) * H + g * R + r0 % R) * D + 8 * cc;
-      const size_t a1 = ((size_t)(b * T + t1r) * H + g * R + r1 % R) * D + 8 * cc;
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      const uint4 x0 = v0 ? ld16u(q + a0) : z, x1 = v1 ? ld16u(q + a1) : z;
-      const uint4 y0 = v0 ? ld16u(dout + a0) : z, y1 = v1 ? ld16u(dout + a1) : z;
-      st16u(&Qs[r0 * LDQ + 8 * cc], x0);
-      st16u(&Qs[r1 * LDQ + 8 * cc], x1);
-      st16u(&dOs[r0 * LDQ + 8 * cc], y0);
-      st16u(&dOs[r1 * LDQ + 8 * cc], y1);
-      const int pos = 32 * (r0 >> 5) + kperm(r0 & 31);
+    s_lim = val ? t - blk * BLK : -1;
+    s_lse = (val && ssub == 0) ? lse[hrow] * LOG2E : INFINITY;
+    s_dd = (val && ssub == 0) ? Dd[hrow] : 0.f;
+  };
+  auto stage_store = [&](int buf) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t a = word_of(x0, m), c = word_of(x1, m);
-        const uint32_t e = word_of(y0, m), f = word_of(y1, m);
-        *reinterpret_cast<uint32_t*>(&QsT[(8 * cc + 2 * m) * LDT + pos]) = pair_lo(a, c);
-        *reinterpret_cast<uint32_t*>(&QsT[(8 * cc + 2 * m + 1) * LDT + pos]) = pair_hi(a, c);
-        *reinterpret_cast<uint32_t*>(&dOsT[(8 * cc + 2 * m) * LDT + pos]) = pair_lo(e, f);
-        *reinterpret_cast<uint32_t*>(&dOsT[(8 * cc + 2 * m + 1) * LDT + pos]) = pair_hi(e, f);
-      }
+    for (int u = 0; u < CPT; ++u) {
+      const int off = srow * D + 8 * swz<DCH>(srow, ssub + 4 * u);
+      st16u(&Qs[buf][off], sq[u]);
+      st16u(&dOs[buf][off], sdo[u]);
     }
-    __syncthreads();
+    if (ssub == 0) {
+      rlse[buf][srow] = s_lse;
+      rdd[buf][srow] = s_dd;
+      rlim[buf][srow] = s_lim;
+      rpair[buf][srow] = s_pair;
+    }
+  };
 
-    // ---- S = Q K^T and dP = dO V^T for the owned keys
-    f32x4 sacc[4][2], pacc[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sacc[mt][0] = sacc[mt][1] = pacc[mt][0] = pacc[mt][1] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 aq = ld8(&Qs[(16 * mt + l16) * LDQ + 32 * ks + 8 * q4]);
-        const bf16x8 ad = ld8(&dOs[(16 * mt + l16) * LDQ + 32 * ks + 8 * q4]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          sacc[mt][nt] = mfma16(aq, bk[nt][ks], sacc[mt][nt]);
-          pacc[mt][nt] = mfma16(ad, bv[nt][ks], pacc[mt][nt]);
-        }
-      }
+  if (ntiles > 0) {
+    stage_load(0);
+    stage_store(0);
+    if (ntiles > 1) stage_load(1);
+  }
+  __syncthreads();
 
-    // ---- P and dS (rows 16mt + 4q4 + e, key kw + 16nt + l16)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * q4 + e;
-        const float lr = lse_s[row], dr = dd_s[row];
-        const int lim = tok_s[row] - blk * BLK;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int key = kw + 16 * nt + l16;
-          const float p = key <= lim ? fast_exp2(sacc[mt][nt][e] * sl2 - lr) : 0.f;
-          sacc[mt][nt][e] = p;
-          pacc[mt][nt][e] = p * (pacc[mt][nt][e] - dr);
-        }
-      }
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int cur = ti & 1;
+    const bf16raw* Qc = Qs[cur];
+    const bf16raw* dOc = dOs[cur];
 
-    // ---- dV += P^T dO, dK += dS^T Q  (owned keys along M, head dim along N, rows as K)
+    // ---- S = Q K^T, dP = dO V^T : two 32-row tiles x the wave's 32 keys
+    f32x16 sacc[2], pacc[2];
+    sacc[0] = sacc[1] = pacc[0] = pacc[1] = zero16();
+    const int kown = kw + l32;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 ap[2], ad[2];
+    for (int ks = 0; ks < KSD; ++ks) {
+      const int ko = kown * D + 8 * swz<DCH>(kown, 2 * ks + h);
+      const bf16x8 bk = ld8(&Ks[ko]), bv = ld8(&Vs[ko]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        ap[nt] = pack_ctiles(sacc[2 * ks][nt], sacc[2 * ks + 1][nt]);
-        ad[nt] = pack_ctiles(pacc[2 * ks][nt], pacc[2 * ks + 1][nt]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const bf16x8 bdo = ld8(&dOsT[(16 * ct + l16) * LDT + 32 * ks + 8 * q4]);
-        const bf16x8 bq = ld8(&QsT[(16 * ct + l16) * LDT + 32 * ks + 8 * q4]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          dva[nt][ct] = mfma16(ap[nt], bdo, dva[nt][ct]);
-          dka[nt][ct] = mfma16(ad[nt], bq, dka[nt][ct]);
-        }
+      for (int rt = 0; rt < 2; ++rt) {
+        const int r = 32 * rt + l32;
+        const int off = r * D + 8 * swz<DCH>(r, 2 * ks + h);
+        sacc[rt] = mfma32(ld8(&Qc[off]), bk, sacc[rt]);
+        pacc[rt] = mfma32(ld8(&dOc[off]), bv, pacc[rt]);
       }
     }
 
-    // ---- dS -> LDS as [row][key in kperm order]
+    // ---- P = exp(scale S - LSE) (masked past the query), dS = P (dP - D)
+    const int key = kw + l32;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 32 * rt + 8 * j + 4 * h;
+        const float4 lv = *reinterpret_cast<const float4*>(&rlse[cur][r0]);
+        const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[cur][r0]);
+        const int4 lm = *reinterpret_cast<const int4*>(&rlim[cur][r0]);
+        const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+        const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dSs[(16 * mt + 4 * q4 + e) * LDS_ + kw + kperm(16 * nt + l16)] = f2bf(pacc[mt][nt][e]);
-    __syncthreads();
-
-    // ---- dQ^T slice = K^T dS^T  (head dim along M, rows along N, all 128 keys as K)
-    f32x4 dq[CW][4];
-#pragma unroll
-    for (int cw = 0; cw < CW; ++cw)
-#pragma unroll
-      for (int n2 = 0; n2 < 4; ++n2) dq[cw][n2] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int n2 = 0; n2 < 4; ++n2) {
-        const bf16x8 bds = ld8(&dSs[(16 * n2 + l16) * LDS_ + 32 * ks + 8 * q4]);
-#pragma unroll
-        for (int cw = 0; cw < CW; ++cw) dq[cw][n2] = mfma16(akt[cw][ks], bds, dq[cw][n2]);
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * j + i;
+          const float p = key <= ma[i] ? fast_exp2(sacc[rt][e] * sl2 - la[i]) : 0.f;
+          sacc[rt][e] = p;
+          pacc[rt][e] = p * (pacc[rt][e] - da[i]);
+        }
       }
+
+    // ---- dV += P^T dO, dK += dS^T Q : owned keys x head dim, rows as K (4 steps of 16)
 #pragma unroll
-    for (int n2 = 0; n2 < 4; ++n2) {
-      const int row = 16 * n2 + l16;
-      const int p = pair_s[row];
+    for (int s = 0; s < 4; ++s) {
+      const int rt = s >> 1, ss = s & 1;
+      const bf16x8 ap = as_bf8(make_uint4(
+          pack2(sacc[rt][8 * ss + 0], sacc[rt][8 * ss + 1]), pack2(sacc[rt][8 * ss + 2], sacc[rt][8 * ss + 3]),
+          pack2(sacc[rt][8 * ss + 4], sacc[rt][8 * ss + 5]), pack2(sacc[rt][8 * ss + 6], sacc[rt][8 * ss + 7])));
+      const bf16x8 ad = as_bf8(make_uint4(
+          pack2(pacc[rt][8 * ss + 0], pacc[rt][8 * ss + 1]), pack2(pacc[rt][8 * ss + 2], pacc[rt][8 * ss + 3]),
+          pack2(pacc[rt][8 * ss + 4], pacc[rt][8 * ss + 5]), pack2(pacc[rt][8 * ss + 6], pacc[rt][8 * ss + 7])));
+      const int ra = 32 * rt + 16 * ss + 4 * h + (i16 >> 2);  // rows of the first transpose read
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int col = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
+        const int ob = (ra + 8) * D + 8 * swz<DCH>(ra + 8, col >> 3) + (col & 7);
+        const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
+        const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
+        dva[ct] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[ct]);
+        dka[ct] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[ct]);
+      }
+    }
+
+    __syncthreads();  // every wave is past the previous tile's dQ (dSt, rpair)
+    // ---- dS^T -> LDS [key][row]: lane holds key kw+l32, rows 32rt + 8j + 4h + (0..3)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 w2 = make_uint2(pack2(pacc[rt][4 * j], pacc[rt][4 * j + 1]),
+                                    pack2(pacc[rt][4 * j + 2], pacc[rt][4 * j + 3]));
+        *reinterpret_cast<uint2*>(&dSt[(kw + l32) * LDT + 32 * rt + 8 * j + 4 * h]) = w2;
+      }
+    if (ti + 1 < ntiles) stage_store(cur ^ 1);
+    __syncthreads();  // dSt and the next tile are in LDS
+    if (ti + 2 < ntiles) stage_load(ti + 2);
+
+    // ---- dQ^T slice = K^T dS^T : head dim along M, rows along N, keys as K (8 steps)
+    const int cw = NCT == 4 ? wave : (wave & 1);
+    const int nt0 = NCT == 4 ? 0 : (wave >> 1);
+    f32x16 dq[QNT];
+#pragma unroll
+    for (int n = 0; n < QNT; ++n) dq[n] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kr = 16 * ks + 8 * h + (i16 >> 2);
+      const int col = 32 * cw + 16 * (g16 & 1) + 4 * (i16 & 3);
+      const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
+      const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
+      const bf16x8 akt = as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+      for (int n = 0; n < QNT; ++n) {
+        const int rc = 32 * (nt0 + n) + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const uint2 b0 = lds_tr4(&dSt[kr * LDT + rc]);
+        const uint2 b1 = lds_tr4(&dSt[(kr + 4) * LDT + rc]);
+        dq[n] = mfma32(akt, as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq[n]);
+      }
+    }
+    // lane holds row 32(nt0+n) + l32, head-dim columns 32cw + 8j + 4h + (0..3)
+#pragma unroll
+    for (int n = 0; n < QNT; ++n) {
+      const int row = 32 * (nt0 + n) + l32;
+      const int p = rpair[cur][row];
       if (p < 0) continue;
-      bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + cbase + 4 * q4;
+      bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * cw + 4 * h;
 #pragma unroll
-      for (int cw = 0; cw < CW; ++cw) {
-        st4bf(dst + 16 * cw, dq[cw][n2][0] * scale, dq[cw][n2][1] * scale, dq[cw][n2][2] * scale,
-              dq[cw][n2][3] * scale);
-      }
+      for (int j = 0; j < 4; ++j)
+        st4bf(dst + 8 * j, dq[n][4 * j] * scale, dq[n][4 * j + 1] * scale, dq[n][4 * j + 2] * scale,
+              dq[n][4 * j + 3] * scale);
     }
-    __syncthreads();
   }
 
-  // ---- dK, dV of the owned keys: lane holds head-dim column 16ct + l16, keys 4q4 + e
+  // ---- dK, dV of the owned keys: lane holds head-dim column 32ct + l32, keys kw + 8j + 4h + i
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const size_t rrow = (kv0 + (size_t)(kw + 16 * nt + 4 * q4 + e) * G) * D + l16;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        dk_acc[rrow + 16 * ct] += scale * dka[nt][ct][e];
-        dv_acc[rrow + 16 * ct] += dva[nt][ct][e];
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int kk = kw + 8 * (e >> 2) + 4 * h + (e & 3);
+      const size_t off = (kv0 + (size_t)kk * G) * D + 32 * ct + l32;
+      dk_acc[off] += scale * dka[ct][e];
+      dv_acc[off] += dva[ct][e];
     }
 }
 
@@ -267,36 +278,39 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const bf16raw* __restrict__ o, 
   if (row < rows && sub == 0) Dd[row] = s;
 }
 
-// dq[b,t,g*R+hh,:] = sum of the token's valid per-slot partials (one wave per token/group).
+// dq[b,t,g*R+hh,:] = sum of the token's valid per-slot partials; one (batch,
+// group, token) row per R*D/8 threads, 16 bytes per thread per slot.
 template <int D, int R>
 __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ idx, const bf16raw* __restrict__ part,
                                                     bf16raw* __restrict__ dq, int T, int H, int G, int K, int t0,
                                                     int W, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int TPR = R * D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int sub = threadIdx.x % TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int bg = row / W, tl = row % W, t = t0 + tl, b = bg / G, g = bg % G;
+  const int hh = sub / (D / 8), c8 = (sub % (D / 8)) * 8;
   const int32_t* ir = idx + ((size_t)bg * T + t) * K;
   const size_t p0 = (size_t)bg * W * K + (size_t)tl * K;
-  const int last = t / BLK;
-  constexpr int NCH = R * D / 4;
-  for (int ch = lane; ch < NCH; ch += 64) {
-    const int hh = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int s = 0; s < K; ++s) {
-      const int bk = ir[s];
-      if (bk < 0 || bk > last) continue;
-      const uint2 raw = *reinterpret_cast<const uint2*>(part + ((p0 + s) * R + hh) * D + c4);
-      a0 += __uint_as_float(raw.x << 16);
-      a1 += __uint_as_float(raw.x & 0xffff0000u);
-      a2 += __uint_as_float(raw.y << 16);
-      a3 += __uint_as_float(raw.y & 0xffff0000u);
+  const unsigned last = (unsigned)(t / BLK);
+  const bf16raw* pp = part + (p0 * R + hh) * D + c8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < K; ++s) {
+    if ((unsigned)ir[s] > last) continue;
+    const uint4 raw = ld16u(pp + (size_t)s * R * D);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] += __uint_as_float(wd[m] << 16);
+      acc[2 * m + 1] += __uint_as_float(wd[m] & 0xffff0000u);
     }
-    uint2 outw;
-    outw.x = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
-    outw.y = (uint32_t)f2bf(a2) | ((uint32_t)f2bf(a3) << 16);
-    *reinterpret_cast<uint2*>(dq + ((size_t)(b * T + t) * H + g * R + hh) * D + c4) = outw;
   }
+  st16u(dq + ((size_t)(b * T + t) * H + g * R + hh) * D + c8,
+        make_uint4(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]), pack2(acc[6], acc[7])));
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, size_t n4) {
@@ -329,7 +343,9 @@ template <int D, int R>
 static hipError_t dq_combine_t(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* dq_part, uint16_t* dq,
                                hipStream_t st) {
   const int rows = g.B * g.G * w.W;
-  k_dq_combine<D, R><<<(rows + 3) / 4, 256, 0, st>>>(idx, dq_part, dq, g.T, g.H, g.G, g.K, w.t0, w.W, rows);
+  constexpr int RPB = 256 / (R * D / 8);
+  k_dq_combine<D, R><<<(rows + RPB - 1) / RPB, 256, 0, st>>>(idx, dq_part, dq, g.T, g.H, g.G, g.K, w.t0, w.W,
+                                                              rows);
   return hipGetLastError();
 }
 

@@ -28,6 +28,36 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef uint16_t bf16raw;
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+// v_mfma_f32_32x32x16_bf16.  A (32 x 16): lane l holds row l%32, K slots
+// 8*(l/32)+e.  B (16 x 32): lane l holds column l%32, same K slots.
+// C (32 x 32): lane l holds column l%32, rows 8*(e/4) + 4*(l/32) + e%4 for
+// e = 0..15.  Elements e = 8s..8s+7 of a C tile are therefore K slots e-8s of
+// a following product that reduces over the C tile's rows, K step s, with
+// slot (h = l/32, e') <-> row 16s + 8*(e'/4) + 4h + e'%4.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// j receives element j%4 of the 8-byte rows read by lanes 4e + j/4, e = 0..3.
+// If lane i of the group points at row (r0 + i/4), columns (n0 + 4*(i%4)) of a
+// row-major bf16 matrix, lane j receives M[r0 + e][n0 + j] for e = 0..3: four
+// consecutive rows of its own column.
+__device__ __forceinline__ uint2 lds_tr4(const void* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -65,9 +95,13 @@ __device__ __forceinline__ bf16raw f2bf(float f) {
 
 __device__ __forceinline__ bf16x8 zero8() { return as_bf8(make_uint4(0u, 0u, 0u, 0u)); }
 
-// Two floats -> one word of two bf16 (round to nearest even), first in the low half.
+// Two floats -> one word of two bf16 (round to nearest even), first in the low
+// half: one v_cvt_pk_bf16_f32.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Pack the C values of two stacked tiles into one bf16 operand.

@@ -16,189 +16,206 @@
 
 namespace msa {
 
+// Position of 16-byte chunk c of row r in a swizzled row-major tile of DCH
+// chunks per row (distinct LDS banks for 16-byte row reads and for transpose
+// reads of 4 rows x 32 bytes).
+template <int DCH>
+__device__ __forceinline__ int fswz(int r, int c) {
+  return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (DCH - 1));
+}
+
+// Each wave owns 32 query rows per tile (one MFMA column tile); the product is
+// taken transposed, S^T = K Q^T with the 128 keys along M, so a lane holds 64
+// keys of one row: the row max and sum are in-lane plus one cross-lane step.
+// P^T then feeds O^T = V^T P^T as the B operand in place; V^T comes from the
+// row-major V tile through LDS transpose reads.
 template <int D, int R>
-__global__ __launch_bounds__(256, 1) void k_fwd_kv(const bf16raw* __restrict__ q, const bf16raw* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q, const bf16raw* __restrict__ k,
                                                    const bf16raw* __restrict__ v, const int4* __restrict__ items,
                                                    const int32_t* __restrict__ item_count,
                                                    const int32_t* __restrict__ list, bf16raw* __restrict__ part_o,
                                                    float* __restrict__ part_lse, int T, int H, int G, int K,
                                                    int t0, int W, int max_items, float scale, float sl2) {
-  constexpr int KS = D / 32;    // k-steps over the head dim
-  constexpr int CT = D / 16;    // output column tiles
-  constexpr int LDK = D + 8;    // K row stride (bf16)
-  constexpr int LDV = BLK + 8;  // V^T row stride (bf16)
+  constexpr int KSD = D / 16;   // 32x32x16 k-steps over the head dim
+  constexpr int NCT = D / 32;   // 32-wide head-dim tiles of O^T
+  constexpr int DCH = D / 8;    // 16-byte chunks per row
   constexpr int TT = 128 / R;   // tokens per 128-row tile
-  __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * LDK];
-  __shared__ __attribute__((aligned(16))) bf16raw Vt[D * LDV];
+  __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
+  __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
 
   const int bg = blockIdx.y;
   if ((int)blockIdx.x >= item_count[bg]) return;
   const int4 it = items[(size_t)bg * max_items + blockIdx.x];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, q4 = lane >> 4;
-  const size_t kv0 = (size_t)(b * T + blk * BLK) * G + g;  // [B*T*G] row of key 0
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const size_t kv0 = (size_t)(b * T + blk * BLK) * G + g;
   const size_t pair0 = (size_t)bg * W * K;
   const int32_t* lst = list + pair0 + start;
 
-  for (int c = threadIdx.x; c < BLK * D / 8; c += 256) {
-    const int r = c / (D / 8), c8 = c % (D / 8);
-    st8(&Ks[r * LDK + 8 * c8], ld8(k + (kv0 + (size_t)r * G) * D + 8 * c8));
+  for (int c = tid; c < BLK * DCH; c += 256) {
+    const int r = c / DCH, cc = c % DCH;
+    const size_t src = (kv0 + (size_t)r * G) * D + 8 * cc;
+    st16u(&Ks[r * D + 8 * fswz<DCH>(r, cc)], ld16u(k + src));
+    st16u(&Vs[r * D + 8 * fswz<DCH>(r, cc)], ld16u(v + src));
   }
-  // V^T: two keys per 32-bit LDS word; keys of each 32-key step stored in kperm order.
-  for (int u = threadIdx.x; u < 64 * (D / 8); u += 256) {
-    const int kpl = u & 15, rest = u >> 4, cc = rest % (D / 8), grp = rest / (D / 8);
-    const int key0 = 32 * grp + 2 * kpl;
-    const uint4 v0 = ld16u(v + (kv0 + (size_t)key0 * G) * D + 8 * cc);
-    const uint4 v1 = ld16u(v + (kv0 + (size_t)(key0 + 1) * G) * D + 8 * cc);
-    const int pos = 32 * grp + kperm(2 * kpl);
+
+  // this lane's query row within a tile and its Q operand (B of S^T: column = row)
+  const int row = 32 * wave + l32;
+  const int tt = row / R, hh = row % R;
+  auto load_q = [&](int ti, bf16x8* bq, int& pr, int& lim) {
+    const int li = ti * TT + tt;
+    const bool val = li < len;
+    pr = val ? lst[li] : -1;
+    const int t = val ? t0 + pr / K : 0;
+    lim = val ? t - blk * BLK : BLK - 1;
+    const bf16raw* qr = q + ((size_t)(b * T + t) * H + g * R + hh) * D + 8 * h;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t a = word_of(v0, m), c = word_of(v1, m);
-      *reinterpret_cast<uint32_t*>(&Vt[(8 * cc + 2 * m) * LDV + pos]) = pair_lo(a, c);
-      *reinterpret_cast<uint32_t*>(&Vt[(8 * cc + 2 * m + 1) * LDV + pos]) = pair_hi(a, c);
-    }
-  }
-  __syncthreads();
+    for (int ks = 0; ks < KSD; ++ks) bq[ks] = val ? ld8(qr + 16 * ks) : zero8();
+  };
 
   const int ntiles = (len + TT - 1) / TT;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    int pr[2], tok[2], hh[2];
-    bool val[2];
-    bf16x8 bq[2][KS];
+  bf16x8 bq[KSD];
+  int pr = -1, lim = BLK - 1;
+  if (ntiles > 0) load_q(0, bq, pr, lim);
+  __syncthreads();
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    // S^T = K Q^T: 4 key tiles of 32 along M, this wave's 32 rows along N
+    f32x16 acc[4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int row = 32 * wave + 16 * nt + l16;
-      const int tt = row / R, li = tile * TT + tt;
-      hh[nt] = row % R;
-      val[nt] = li < len;
-      pr[nt] = val[nt] ? lst[li] : 0;
-      tok[nt] = t0 + pr[nt] / K;
-      const bf16raw* qr = q + ((size_t)(b * T + tok[nt]) * H + g * R + hh[nt]) * D + 8 * q4;
+    for (int kt = 0; kt < 4; ++kt) acc[kt] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bq[nt][ks] = val[nt] ? ld8(qr + 32 * ks) : zero8();
+    for (int ks = 0; ks < KSD; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int kr = 32 * kt + l32;
+        acc[kt] = mfma32(ld8(&Ks[kr * D + 8 * fswz<DCH>(kr, 2 * ks + h)]), bq[ks], acc[kt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the K operand loads of later steps from piling up in registers
+    }
+    const int cpr = pr, clim = lim;
+
+    // softmax over the block's keys of this row: lane holds keys 32kt + 8j + 4h + i
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3);
+        const float sv = kk > clim ? -INFINITY : acc[kt][e];
+        acc[kt][e] = sv;
+        m = fmaxf(m, sv);
+      }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float ms = m * sl2;
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = fast_exp2(acc[kt][e] * sl2 - ms);
+        acc[kt][e] = pv;
+        l += pv;
+      }
+    l += __shfl_xor(l, 32);
+
+    // P^T as bf16 B operands (K step s = keys of tile s/2, C elements 8(s%2)..+7)
+    bf16x8 bp[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int kt = s >> 1, ss = s & 1;
+      bp[s] = as_bf8(make_uint4(
+          pack2(acc[kt][8 * ss + 0], acc[kt][8 * ss + 1]), pack2(acc[kt][8 * ss + 2], acc[kt][8 * ss + 3]),
+          pack2(acc[kt][8 * ss + 4], acc[kt][8 * ss + 5]), pack2(acc[kt][8 * ss + 6], acc[kt][8 * ss + 7])));
     }
 
-    // S^T = K Q^T : keys along M (8 tiles), this wave's 32 rows along N (2 tiles)
-    f32x4 acc[8][2];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt][0] = acc[mt][1] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 a = ld8(&Ks[(16 * mt + l16) * LDK + 32 * ks + 8 * q4]);
-        acc[mt][0] = mfma16(a, bq[0][ks], acc[mt][0]);
-        acc[mt][1] = mfma16(a, bq[1][ks], acc[mt][1]);
-      }
+    if (ti + 1 < ntiles) load_q(ti + 1, bq, pr, lim);  // next tile's rows in flight during PV
 
-    float mrow[2], lrow[2];
+    // O^T = V^T P^T: head dim along M (NCT tiles), rows along N, keys as K (8 steps of 16)
+    f32x16 oacc[NCT];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int lim = val[nt] ? tok[nt] - blk * BLK : BLK - 1;  // keys past the query are masked
-      float m = -INFINITY;
+    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = zero16();
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+    for (int s = 0; s < 8; ++s) {
+      const int kt = s >> 1, ss = s & 1;
+      const int kr = 32 * kt + 16 * ss + 4 * h + (i16 >> 2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = acc[mt][nt][e];
-          if (16 * mt + 4 * q4 + e > lim) s = -INFINITY;
-          acc[mt][nt][e] = s;
-          m = fmaxf(m, s);
-        }
-      m = wave_max_xor_16_32(m);
-      const float ms = m * sl2;
-      float l = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(acc[mt][nt][e] * sl2 - ms);
-          acc[mt][nt][e] = p;
-          l += p;
-        }
-      mrow[nt] = m;
-      lrow[nt] = wave_sum_xor_16_32(l);
-    }
-
-    // O^T = V^T P^T : head dim along M (CT tiles), rows along N, keys as K (4 steps)
-    f32x4 oacc[CT][2];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) oacc[ct][0] = oacc[ct][1] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 p0 = pack_ctiles(acc[2 * ks][0], acc[2 * ks + 1][0]);
-      const bf16x8 p1 = pack_ctiles(acc[2 * ks][1], acc[2 * ks + 1][1]);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const bf16x8 a = ld8(&Vt[(16 * ct + l16) * LDV + 32 * ks + 8 * q4]);
-        oacc[ct][0] = mfma16(a, p0, oacc[ct][0]);
-        oacc[ct][1] = mfma16(a, p1, oacc[ct][1]);
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int col = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const uint2 a0 = lds_tr4(&Vs[kr * D + 8 * fswz<DCH>(kr, col >> 3) + (col & 7)]);
+        const uint2 a1 = lds_tr4(&Vs[(kr + 8) * D + 8 * fswz<DCH>(kr + 8, col >> 3) + (col & 7)]);
+        oacc[ct] = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), bp[s], oacc[ct]);
       }
     }
 
+    // lane holds row `row`, head-dim columns 32ct + 8j + 4h + (0..3)
+    if (cpr >= 0) {
+      const float inv = 1.0f / l;
+      const size_t pidx = pair0 + (size_t)cpr;
+      bf16raw* dst = part_o + (pidx * R + hh) * D + 4 * h;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (!val[nt]) continue;
-      const float inv = 1.0f / lrow[nt];
-      const size_t pidx = pair0 + (size_t)pr[nt];
-      bf16raw* dst = part_o + (pidx * R + hh[nt]) * D + 4 * q4;
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        st4bf(dst + 16 * ct, oacc[ct][nt][0] * inv, oacc[ct][nt][1] * inv, oacc[ct][nt][2] * inv,
-              oacc[ct][nt][3] * inv);
-      }
-      if (q4 == 0) part_lse[pidx * R + hh[nt]] = mrow[nt] * scale + fast_log2(lrow[nt]) * LN2;
+        for (int j = 0; j < 4; ++j)
+          st4bf(dst + 32 * ct + 8 * j, oacc[ct][4 * j] * inv, oacc[ct][4 * j + 1] * inv, oacc[ct][4 * j + 2] * inv,
+                oacc[ct][4 * j + 3] * inv);
+      if (h == 0) part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;
     }
   }
 }
 
-// One wavefront per (batch, group, token): exact log-sum-exp merge of the
-// token's per-block partials.  A slot holds a partial iff its cache entry is a
-// valid causal block.  A row with no valid entry gets O = 0, LSE = -inf.
+// Exact log-sum-exp merge of a token's per-block partials, one (batch,
+// group, token) row per R*D/8 threads (each thread owns 8 head-dim values of
+// one head and streams 16 bytes per slot).  A slot holds a partial iff its
+// cache entry is a valid causal block.  A row with no valid entry gets
+// O = 0, LSE = -inf.
 template <int D, int R>
 __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__ idx, const bf16raw* __restrict__ part_o,
                                                      const float* __restrict__ part_lse, bf16raw* __restrict__ o,
                                                      float* __restrict__ lse, int T, int H, int G, int K, int t0,
                                                      int W, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int TPR = R * D / 8;  // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
+  const int sub = threadIdx.x % TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int bg = row / W, tl = row % W, t = t0 + tl, b = bg / G, g = bg % G;
+  const int hh = sub / (D / 8), c8 = (sub % (D / 8)) * 8;
   const int32_t* ir = idx + ((size_t)bg * T + t) * K;
   const size_t p0 = (size_t)bg * W * K + (size_t)tl * K;
-  const int last = t / BLK;
-  constexpr int NCH = R * D / 4;
-  for (int ch = lane; ch < NCH; ch += 64) {
-    const int hh = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
-    float M = -INFINITY;
+  const unsigned last = (unsigned)(t / BLK);
+  const float* pl = part_lse + p0 * R + hh;
+  const bf16raw* po = part_o + (p0 * R + hh) * D + c8;
+
+  float M = -INFINITY;
+  for (int s = 0; s < K; ++s)
+    if ((unsigned)ir[s] <= last) M = fmaxf(M, pl[(size_t)s * R]);
+  float L = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (M != -INFINITY) {
+    const float Ml = M * LOG2E;
+#pragma unroll 4
     for (int s = 0; s < K; ++s) {
-      const int bk = ir[s];
-      if (bk >= 0 && bk <= last) M = fmaxf(M, part_lse[(p0 + s) * R + hh]);
-    }
-    float L = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    if (M != -INFINITY) {
-      const float Ml = M * LOG2E;
-      for (int s = 0; s < K; ++s) {
-        const int bk = ir[s];
-        if (bk < 0 || bk > last) continue;
-        const float w = fast_exp2(part_lse[(p0 + s) * R + hh] * LOG2E - Ml);
-        const uint2 raw = *reinterpret_cast<const uint2*>(part_o + ((p0 + s) * R + hh) * D + c4);
-        L += w;
-        a0 += w * __uint_as_float(raw.x << 16);
-        a1 += w * __uint_as_float(raw.x & 0xffff0000u);
-        a2 += w * __uint_as_float(raw.y << 16);
-        a3 += w * __uint_as_float(raw.y & 0xffff0000u);
+      if ((unsigned)ir[s] > last) continue;
+      const float w = fast_exp2(pl[(size_t)s * R] * LOG2E - Ml);
+      const uint4 raw = ld16u(po + (size_t)s * R * D);
+      L += w;
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[2 * m] += w * __uint_as_float(wd[m] << 16);
+        acc[2 * m + 1] += w * __uint_as_float(wd[m] & 0xffff0000u);
       }
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const size_t orow = ((size_t)(b * T + t) * H + g * R + hh);
-    uint2 outw;
-    outw.x = (uint32_t)f2bf(a0 * inv) | ((uint32_t)f2bf(a1 * inv) << 16);
-    outw.y = (uint32_t)f2bf(a2 * inv) | ((uint32_t)f2bf(a3 * inv) << 16);
-    *reinterpret_cast<uint2*>(o + orow * D + c4) = outw;
-    if (c4 == 0) lse[orow] = L > 0.f ? M + fast_log2(L) * LN2 : -INFINITY;
   }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const size_t orow = (size_t)(b * T + t) * H + g * R + hh;
+  st16u(o + orow * D + c8, make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
+                                      pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv)));
+  if (c8 == 0) lse[orow] = L > 0.f ? M + fast_log2(L) * LN2 : -INFINITY;
 }
 
 template <int D, int R>
@@ -214,8 +231,9 @@ template <int D, int R>
 static hipError_t fwd_combine_t(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* part_o,
                                 const float* part_lse, uint16_t* o, float* lse, hipStream_t st) {
   const int rows = g.B * g.G * w.W;
-  k_fwd_combine<D, R><<<(rows + 3) / 4, 256, 0, st>>>(idx, part_o, part_lse, o, lse, g.T, g.H, g.G, g.K, w.t0,
-                                                       w.W, rows);
+  constexpr int RPB = 256 / (R * D / 8);
+  k_fwd_combine<D, R><<<(rows + RPB - 1) / RPB, 256, 0, st>>>(idx, part_o, part_lse, o, lse, g.T, g.H, g.G, g.K,
+                                                               w.t0, w.W, rows);
   return hipGetLastError();
 }
 

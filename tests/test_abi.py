@@ -1,0 +1,167 @@
+"""Host-side tests of libmsa's C ABI (no GPU needed).
+
+The library must load, export every function include/msa.h declares, and
+reject bad arguments synchronously with the documented status codes before
+anything reaches the GPU.  Every call below fails a host check, so no kernel
+is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def msa():
+    import block_sparse_attention_qk_amd as m
+    if not os.path.exists(m.lib_path()):
+        from block_sparse_attention_qk_amd import build
+        build.build()
+    m.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def lib(msa):
+    return msa.load()
+
+
+def _dims(msa, B=1, T=1024, H=8, G=2, d=128, dp=64, topk=4, scale=0.0):
+    return msa._dims(B, T, H, G, d, dp, topk, scale)
+
+
+def test_exports_every_declared_function(lib, msa):
+    header = open(os.path.join(ROOT, "include", "msa.h")).read()
+    declared = set(re.findall(r"^[A-Za-z_][\w \*]*?\b(msa_\w+)\s*\(", header, flags=re.M))
+    assert declared, "no declarations parsed"
+    assert declared == set(msa.EXPORTED_SYMBOLS), declared ^ set(msa.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.msa_version().decode().startswith("msa-gfx950")
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(7):
+        s = lib.msa_status_str(code)
+        assert s and s.decode() not in seen
+        seen.add(s.decode())
+    assert lib.msa_status_str(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=1000), ERR_SHAPE),           # not a multiple of 128
+    (dict(T=0), ERR_SHAPE),
+    (dict(T=1 << 21), ERR_SHAPE),        # above the supported length
+    (dict(B=0), ERR_SHAPE),
+    (dict(topk=0), ERR_SHAPE),
+    (dict(topk=1025), ERR_SHAPE),
+    (dict(H=6, G=4), ERR_SHAPE),         # H % G != 0
+    (dict(H=6, G=2), ERR_UNSUP),         # R = 3
+    (dict(H=64, G=2), ERR_UNSUP),        # R = 32
+    (dict(d=96), ERR_UNSUP),
+    (dict(scale=float("nan")), ERR_SHAPE),
+])
+def test_main_branch_rejects_bad_dims(lib, msa, kw, code):
+    d = _dims(msa, **kw)
+    P = ctypes.c_void_p(4096)
+    assert lib.msa_fwd(ctypes.byref(d), P, P, P, P, P, P, P, 1 << 40, None) == code
+    assert lib.msa_bwd(ctypes.byref(d), P, P, P, P, P, P, P, P, P, P, P, 1 << 40, None) == code
+    assert lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_FWD) == 0
+    assert lib.msa_workspace_min_bytes(ctypes.byref(d), msa.OP_BWD) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dp=48), ERR_UNSUP),
+    (dict(dp=256), ERR_UNSUP),
+    (dict(T=200), ERR_SHAPE),
+    (dict(G=0), ERR_SHAPE),
+])
+def test_select_rejects_bad_dims(lib, msa, kw, code):
+    d = _dims(msa, **kw)
+    P = ctypes.c_void_p(4096)
+    assert lib.msa_proxy_select(ctypes.byref(d), P, P, P, P, 1 << 40, None) == code
+
+
+def test_select_ignores_main_branch_dims(lib, msa):
+    # H and d do not enter the Index Branch: an odd head count is fine there,
+    # the call still stops at the (deliberately) missing workspace.
+    d = _dims(msa, H=3, d=96)
+    P = ctypes.c_void_p(4096)
+    assert lib.msa_proxy_select(ctypes.byref(d), P, P, P, P, 0, None) == ERR_WS
+
+
+def test_null_dims_and_pointers(lib, msa):
+    P = ctypes.c_void_p(4096)
+    assert lib.msa_fwd(None, P, P, P, P, P, P, P, 1 << 40, None) == ERR_NULL
+    d = _dims(msa)
+    for i in range(7):
+        args = [P] * 7
+        args[i] = None
+        assert lib.msa_fwd(ctypes.byref(d), *args, 1 << 40, None) == ERR_NULL, i
+    for i in range(11):
+        args = [P] * 11
+        args[i] = None
+        assert lib.msa_bwd(ctypes.byref(d), *args, 1 << 40, None) == ERR_NULL, i
+    for i in range(4):
+        args = [P] * 4
+        args[i] = None
+        assert lib.msa_proxy_select(ctypes.byref(d), *args, 1 << 40, None) == ERR_NULL, i
+
+
+def test_misaligned_pointers(lib, msa):
+    d = _dims(msa)
+    P, Q = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    for i in range(7):
+        args = [P] * 7
+        args[i] = Q
+        assert lib.msa_fwd(ctypes.byref(d), *args, 1 << 40, None) == ERR_ALIGN, i
+    for i in range(4):
+        args = [P] * 4
+        args[i] = Q
+        assert lib.msa_proxy_select(ctypes.byref(d), *args, 1 << 40, None) == ERR_ALIGN, i
+
+
+def test_workspace_too_small(lib, msa):
+    d = _dims(msa)
+    P = ctypes.c_void_p(4096)
+    for op, call in ((msa.OP_SELECT, lambda n: lib.msa_proxy_select(ctypes.byref(d), P, P, P, P, n, None)),
+                     (msa.OP_FWD, lambda n: lib.msa_fwd(ctypes.byref(d), P, P, P, P, P, P, P, n, None)),
+                     (msa.OP_BWD, lambda n: lib.msa_bwd(ctypes.byref(d), P, P, P, P, P, P, P, P, P, P, P, n,
+                                                       None))):
+        need = lib.msa_workspace_min_bytes(ctypes.byref(d), op)
+        assert need > 0
+        assert call(need - 1) == ERR_WS
+        assert call(0) == ERR_WS
+
+
+def test_workspace_sizes(msa):
+    for name, shape in (("tiny", (1, 1024, 4, 1, 64, 32, 4)), ("128k", (1, 131072, 32, 4, 128, 64, 32)),
+                        ("1m", (1, 1 << 20, 16, 2, 128, 64, 288))):
+        for op in (msa.OP_SELECT, msa.OP_FWD, msa.OP_BWD):
+            full = msa.msa_workspace_bytes(*shape, op)
+            lo = msa.msa_workspace_min_bytes(*shape, op)
+            assert 0 < lo <= full, (name, op)
+            assert full <= (40 << 30) + (16 << 30), (name, op, full)  # capped (plus T-sized accumulators)
+    # 128K runs the main branch in one window: the pair partials of all tokens fit.
+    B, T, H, G, d, dp, k = 1, 131072, 32, 4, 128, 64, 32
+    pairs_bytes = B * G * T * k * (H // G) * d * 2
+    assert msa.msa_workspace_bytes(B, T, H, G, d, dp, k, msa.OP_FWD) > pairs_bytes
+
+
+def test_binding_rejects_host_tensors(msa):
+    x = torch.zeros((1, 256, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        msa.msa_proxy_select(x, x, 2)
+    with pytest.raises(TypeError):
+        msa.msa_proxy_select(x.float(), x, 2)
+    q = torch.zeros((1, 256, 4, 64), dtype=torch.bfloat16)
+    idx = torch.zeros((1, 2, 256, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        msa.msa_fwd(q, x, x, idx)
