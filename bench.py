@@ -212,6 +212,8 @@ def main() -> int:
     ap.add_argument("--also", default="1m", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference kernel for traffic counters)")
     ap.add_argument("--gpu-inputs", action="store_true",
                     help="draw the main workload's inputs on the GPU (same recipe, different stream; for profiling)")
     args = ap.parse_args()
@@ -223,6 +225,13 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     msa.load()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = synth.CONFIGS[args.config]
     print("bench: %s steps=%d warmup=%d" % (cfg, args.steps, args.warmup), file=sys.stderr, flush=True)
     main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=not args.gpu_inputs)

@@ -25,6 +25,7 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # keep the compiler from emitting packed fp32 vector ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",  # MFMA results in VGPRs: no AGPR round trips before VALU use
     "-Wall", "-Wno-unused-function",
 ]
 

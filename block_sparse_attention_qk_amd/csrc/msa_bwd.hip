@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     }
     s_lim = val ? t - blk * BLK : -1;
     s_lse = (val && ssub == 0) ? lse[hrow] * LOG2E : INFINITY;
-    s_dd = (val && ssub == 0) ? Dd[hrow] : 0.f;
+    s_dd = (val && ssub == 0) ? Dd[hrow] * scale : 0.f;
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
@@ -124,36 +124,49 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
   if (ntiles > 0) {
     stage_load(0);
     stage_store(0);
-    if (ntiles > 1) stage_load(1);
+    stage_load(1);  // rows past the list load as zeros
   }
   __syncthreads();
 
+  const int kown = kw + l32;
+  const int cw = NCT == 4 ? wave : (wave & 1);
+  const int nt0 = NCT == 4 ? 0 : (wave >> 1);
+  // A operands of dQ^T = K^T dS^T for this wave's head-dim slice, all 128 keys (8 k-steps)
+  bf16x8 akt[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int kr = 16 * ks + 8 * h + (i16 >> 2);
+    const int col = 32 * cw + 16 * (g16 & 1) + 4 * (i16 & 3);
+    const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
+    const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
+    akt[ks] = as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+  }
   for (int ti = 0; ti < ntiles; ++ti) {
     const int cur = ti & 1;
     const bf16raw* Qc = Qs[cur];
     const bf16raw* dOc = dOs[cur];
+    uint2 dsw[2][4];  // dS as bf16 pairs, kept for the LDS exchange
 
-    // ---- S = Q K^T, dP = dO V^T : two 32-row tiles x the wave's 32 keys
-    f32x16 sacc[2], pacc[2];
-    sacc[0] = sacc[1] = pacc[0] = pacc[1] = zero16();
-    const int kown = kw + l32;
+    bf16x8 bk[KSD], bv[KSD];  // own-key K/V operands, shared by both row tiles
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       const int ko = kown * D + 8 * swz<DCH>(kown, 2 * ks + h);
-      const bf16x8 bk = ld8(&Ks[ko]), bv = ld8(&Vs[ko]);
+      bk[ks] = ld8(&Ks[ko]);
+      bv[ks] = ld8(&Vs[ko]);
+    }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < 2; ++rt) {
+      // ---- S = Q K^T, dP = dO V^T : 32 rows x the wave's 32 keys
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
         const int r = 32 * rt + l32;
         const int off = r * D + 8 * swz<DCH>(r, 2 * ks + h);
-        sacc[rt] = mfma32(ld8(&Qc[off]), bk, sacc[rt]);
-        pacc[rt] = mfma32(ld8(&dOc[off]), bv, pacc[rt]);
+        sacc = mfma32(ld8(&Qc[off]), bk[ks], sacc);
+        pacc = mfma32(ld8(&dOc[off]), bv[ks], pacc);
       }
-    }
-
-    // ---- P = exp(scale S - LSE) (masked past the query), dS = P (dP - D)
-    const int key = kw + l32;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+      // ---- P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D): the
+      // softmax scale of both dK and dQ is folded in here; branch-free
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r0 = 32 * rt + 8 * j + 4 * h;
@@ -165,68 +178,59 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * j + i;
-          const float p = key <= ma[i] ? fast_exp2(sacc[rt][e] * sl2 - la[i]) : 0.f;
-          sacc[rt][e] = p;
-          pacc[rt][e] = p * (pacc[rt][e] - da[i]);
+          const float ex = fast_exp2(sacc[e] * sl2 - la[i]);
+          const float pv = kown <= ma[i] ? ex : 0.f;
+          sacc[e] = pv;
+          pacc[e] = pv * fmaf(pacc[e], scale, -da[i]);
         }
+        dsw[rt][j] = make_uint2(pack2(pacc[4 * j], pacc[4 * j + 1]), pack2(pacc[4 * j + 2], pacc[4 * j + 3]));
       }
-
-    // ---- dV += P^T dO, dK += dS^T Q : owned keys x head dim, rows as K (4 steps of 16)
+      // ---- dV += P^T dO, dK += dS^T Q for the two 16-row K steps of this row tile
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int rt = s >> 1, ss = s & 1;
-      const bf16x8 ap = as_bf8(make_uint4(
-          pack2(sacc[rt][8 * ss + 0], sacc[rt][8 * ss + 1]), pack2(sacc[rt][8 * ss + 2], sacc[rt][8 * ss + 3]),
-          pack2(sacc[rt][8 * ss + 4], sacc[rt][8 * ss + 5]), pack2(sacc[rt][8 * ss + 6], sacc[rt][8 * ss + 7])));
-      const bf16x8 ad = as_bf8(make_uint4(
-          pack2(pacc[rt][8 * ss + 0], pacc[rt][8 * ss + 1]), pack2(pacc[rt][8 * ss + 2], pacc[rt][8 * ss + 3]),
-          pack2(pacc[rt][8 * ss + 4], pacc[rt][8 * ss + 5]), pack2(pacc[rt][8 * ss + 6], pacc[rt][8 * ss + 7])));
-      const int ra = 32 * rt + 16 * ss + 4 * h + (i16 >> 2);  // rows of the first transpose read
+      for (int ss = 0; ss < 2; ++ss) {
+        const bf16x8 ap = as_bf8(make_uint4(
+            pack2(sacc[8 * ss + 0], sacc[8 * ss + 1]), pack2(sacc[8 * ss + 2], sacc[8 * ss + 3]),
+            pack2(sacc[8 * ss + 4], sacc[8 * ss + 5]), pack2(sacc[8 * ss + 6], sacc[8 * ss + 7])));
+        const bf16x8 ad = as_bf8(make_uint4(dsw[rt][2 * ss].x, dsw[rt][2 * ss].y, dsw[rt][2 * ss + 1].x,
+                                            dsw[rt][2 * ss + 1].y));
+        const int ra = 32 * rt + 16 * ss + 4 * h + (i16 >> 2);  // rows of the first transpose read
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int col = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
-        const int ob = (ra + 8) * D + 8 * swz<DCH>(ra + 8, col >> 3) + (col & 7);
-        const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
-        const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
-        dva[ct] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[ct]);
-        dka[ct] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int col = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+          const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
+          const int ob = (ra + 8) * D + 8 * swz<DCH>(ra + 8, col >> 3) + (col & 7);
+          const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
+          const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
+          dva[ct] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[ct]);
+          dka[ct] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[ct]);
+        }
       }
     }
 
     __syncthreads();  // every wave is past the previous tile's dQ (dSt, rpair)
-    // ---- dS^T -> LDS [key][row]: lane holds key kw+l32, rows 32rt + 8j + 4h + (0..3)
+    // ---- dS^T -> LDS [key][row]: lane holds key kown, rows 32rt + 8j + 4h + (0..3)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint2 w2 = make_uint2(pack2(pacc[rt][4 * j], pacc[rt][4 * j + 1]),
-                                    pack2(pacc[rt][4 * j + 2], pacc[rt][4 * j + 3]));
-        *reinterpret_cast<uint2*>(&dSt[(kw + l32) * LDT + 32 * rt + 8 * j + 4 * h]) = w2;
-      }
-    if (ti + 1 < ntiles) stage_store(cur ^ 1);
-    __syncthreads();  // dSt and the next tile are in LDS
-    if (ti + 2 < ntiles) stage_load(ti + 2);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(&dSt[kown * LDT + 32 * rt + 8 * j + 4 * h]) = dsw[rt][j];
+    stage_store(cur ^ 1);  // tile ti+1 (zeros past the list)
+    __syncthreads();       // dSt and the next tile are in LDS
+    stage_load(ti + 2);
 
     // ---- dQ^T slice = K^T dS^T : head dim along M, rows along N, keys as K (8 steps)
-    const int cw = NCT == 4 ? wave : (wave & 1);
-    const int nt0 = NCT == 4 ? 0 : (wave >> 1);
     f32x16 dq[QNT];
 #pragma unroll
     for (int n = 0; n < QNT; ++n) dq[n] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int kr = 16 * ks + 8 * h + (i16 >> 2);
-      const int col = 32 * cw + 16 * (g16 & 1) + 4 * (i16 & 3);
-      const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
-      const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
-      const bf16x8 akt = as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y));
 #pragma unroll
       for (int n = 0; n < QNT; ++n) {
         const int rc = 32 * (nt0 + n) + 16 * (g16 & 1) + 4 * (i16 & 3);
         const uint2 b0 = lds_tr4(&dSt[kr * LDT + rc]);
         const uint2 b1 = lds_tr4(&dSt[(kr + 4) * LDT + rc]);
-        dq[n] = mfma32(akt, as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq[n]);
+        dq[n] = mfma32(akt[ks], as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq[n]);
       }
     }
     // lane holds row 32(nt0+n) + l32, head-dim columns 32cw + 8j + 4h + (0..3)
@@ -234,12 +238,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     for (int n = 0; n < QNT; ++n) {
       const int row = 32 * (nt0 + n) + l32;
       const int p = rpair[cur][row];
-      if (p < 0) continue;
-      bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * cw + 4 * h;
+      if (p >= 0) {
+        bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * cw + 4 * h;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        st4bf(dst + 8 * j, dq[n][4 * j] * scale, dq[n][4 * j + 1] * scale, dq[n][4 * j + 2] * scale,
-              dq[n][4 * j + 3] * scale);
+        for (int j = 0; j < 4; ++j)
+          st4bf(dst + 8 * j, dq[n][4 * j], dq[n][4 * j + 1], dq[n][4 * j + 2], dq[n][4 * j + 3]);
+      }
     }
   }
 
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     for (int e = 0; e < 16; ++e) {
       const int kk = kw + 8 * (e >> 2) + 4 * h + (e & 3);
       const size_t off = (kv0 + (size_t)kk * G) * D + 32 * ct + l32;
-      dk_acc[off] += scale * dka[ct][e];
+      dk_acc[off] += dka[ct][e];
       dv_acc[off] += dva[ct][e];
     }
 }
@@ -298,15 +302,23 @@ __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ 
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < K; ++s) {
-    if ((unsigned)ir[s] > last) continue;
-    const uint4 raw = ld16u(pp + (size_t)s * R * D);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
+  for (int s0 = 0; s0 < K; s0 += SB) {
+    uint4 raw[SB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc[2 * m] += __uint_as_float(wd[m] << 16);
-      acc[2 * m + 1] += __uint_as_float(wd[m] & 0xffff0000u);
+    for (int u = 0; u < SB; ++u) {
+      const int s = s0 + u;
+      const bool ok = s < K && (unsigned)ir[s] <= last;
+      raw[u] = ok ? ld16u(pp + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[2 * m] += __uint_as_float(wd[m] << 16);
+        acc[2 * m + 1] += __uint_as_float(wd[m] & 0xffff0000u);
+      }
     }
   }
   st16u(dq + ((size_t)(b * T + t) * H + g * R + hh) * D + c8,

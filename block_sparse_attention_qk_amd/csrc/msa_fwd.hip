@@ -189,25 +189,39 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   const float* pl = part_lse + p0 * R + hh;
   const bf16raw* po = part_o + (p0 * R + hh) * D + c8;
 
+  constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
   float M = -INFINITY;
-  for (int s = 0; s < K; ++s)
-    if ((unsigned)ir[s] <= last) M = fmaxf(M, pl[(size_t)s * R]);
+  for (int s0 = 0; s0 < K; s0 += SB) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int s = s0 + u;
+      if (s < K && (unsigned)ir[s] <= last) M = fmaxf(M, pl[(size_t)s * R]);
+    }
+  }
   float L = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (M != -INFINITY) {
     const float Ml = M * LOG2E;
-#pragma unroll 4
-    for (int s = 0; s < K; ++s) {
-      if ((unsigned)ir[s] > last) continue;
-      const float w = fast_exp2(pl[(size_t)s * R] * LOG2E - Ml);
-      const uint4 raw = ld16u(po + (size_t)s * R * D);
-      L += w;
-      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int s0 = 0; s0 < K; s0 += SB) {
+      float w[SB];
+      uint4 raw[SB];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[2 * m] += w * __uint_as_float(wd[m] << 16);
-        acc[2 * m + 1] += w * __uint_as_float(wd[m] & 0xffff0000u);
+      for (int u = 0; u < SB; ++u) {
+        const int s = s0 + u;
+        const bool ok = s < K && (unsigned)ir[s] <= last;
+        w[u] = ok ? fast_exp2(pl[(size_t)s * R] * LOG2E - Ml) : 0.f;
+        raw[u] = ok ? ld16u(po + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        L += w[u];
+        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc[2 * m] += w[u] * __uint_as_float(wd[m] << 16);
+          acc[2 * m + 1] += w[u] * __uint_as_float(wd[m] & 0xffff0000u);
+        }
       }
     }
   }

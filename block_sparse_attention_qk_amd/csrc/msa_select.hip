@@ -160,6 +160,25 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
     key[i] = kk;
   }
 
+  uint32_t prefix = 0;
+  int need = nsel;  // rank of the wanted key among keys matching prefix
+  if constexpr (VPL <= 16) {
+    // Short rows: build the k-th largest key bit by bit from the top; each
+    // step is one ballot count per register of keys.
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i * 64 < nc) cnt += __popcll(__ballot((i * 64 + lane < nc) && key[i] >= cand));
+      if (cnt >= nsel) prefix = cand;
+    }
+    int cnt_gt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i * 64 < nc) cnt_gt += __popcll(__ballot((i * 64 + lane < nc) && key[i] > prefix));
+    need = nsel - cnt_gt;
+  } else {
   // Radix select of the nsel-th largest key.  Pooled scores of a row share
   // their sign and exponent bits, so the digits start below the common prefix
   // of the row's smallest and largest key (otherwise every key would fall into
@@ -180,8 +199,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
   }
   const uint32_t diff = kmin ^ kmax;
   int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // low bits still undecided
-  uint32_t prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
-  int need = nsel;  // rank of the wanted key among keys matching prefix
+  prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
   while (bits > 0) {
     const int width = bits < 11 ? bits : 11;
     const int sh = bits - width, nbins = 1 << width;
@@ -222,6 +240,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
     prefix |= (uint32_t)bin << sh;
     bits = sh;
     __builtin_amdgcn_wave_barrier();
+  }
   }
   const uint32_t kth = prefix;
   const int need_eq = need;  // equal keys to take, lowest block index first
