@@ -4,18 +4,17 @@
 // keyed on the cached block indices, xcelit "How MSA works").
 //
 // KV-stationary schedule, one work item per (batch, group, block) and window.
-// Each of the 4 waves owns 32 keys of the block: their K and V rows stay in
-// registers as MFMA operands and their dK/dV accumulate in registers over all
-// pairs that read the block.  Tiles of 64 query rows (64/R tokens x R heads)
-// stream through a double-buffered LDS tile in plain row-major form; the
-// global loads of tile i+2 are in flight while tile i computes.  Per tile
-// (v_mfma_f32_32x32x16_bf16 throughout):
-//   S = Q K^T, dP = dO V^T           (rows along M, owned keys along N)
-//   P = exp(scale S - LSE), dS = P (dP - D)
-//   dV += P^T dO, dK += dS^T Q        (P, dS reused in place as A operands;
-//                                      dO, Q read with LDS transpose reads)
-//   dQ^T = K^T dS^T                   (dS^T exchanged through LDS; each wave
-//                                      makes one 32-wide slice of dQ)
+// Eight waves (two per SIMD) share one 128-key block; wave (kq, hf) owns keys
+// [32kq, 32kq+32) and half hf of the tile rows and of the head dim.  Tiles of
+// 64 query rows (64/R tokens x R heads) stream through double-buffered LDS in
+// plain row-major form; the global loads of tile i+2 are in flight while tile
+// i computes.  Per tile (v_mfma_f32_32x32x16_bf16 throughout):
+//   S = Q K^T, dP = dO V^T        own 32 rows x own 32 keys
+//   P = exp(scale S - LSE), dS = scale P (dP - D)
+//   P^T, dS^T -> LDS              (so the other half's rows are visible)
+//   dV += P^T dO, dK += dS^T Q    own keys x own half of the head dim, all
+//                                 64 rows (dO, Q by LDS transpose reads)
+//   dQ^T = K^T dS^T               one 32 x 32 (head dim x rows) tile per wave
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
 // token's partials.  dK/dV are added into fp32 accumulators once per item.
 // Nothing is accumulated with atomics.
@@ -34,8 +33,10 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (DCH - 1));
 }
 
+constexpr int BWD_THREADS = 512;
+
 template <int D, int R>
-__global__ __launch_bounds__(256, 1) void k_bwd_kv(
+__global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
     const bf16raw* __restrict__ q, const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
     const bf16raw* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int4* __restrict__ items, const int32_t* __restrict__ item_count, const int32_t* __restrict__ list,
@@ -43,19 +44,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     int K, int t0, int W, int max_items, float scale, float sl2) {
   constexpr int KSD = D / 16;    // 32x32x16 k-steps over the head dim
   constexpr int NCT = D / 32;    // 32-wide head-dim tiles
+  constexpr int HCT = NCT / 2;   // head-dim tiles of dK/dV per wave
   constexpr int DCH = D / 8;     // 16-byte chunks per row
   constexpr int TR = 64;         // query rows per tile
   constexpr int TT = TR / R;     // tokens per tile
-  constexpr int CPT = DCH / 4;   // chunks per thread per staged matrix (thread = one row)
-  constexpr int LDT = TR + 8;    // dS^T row stride (bf16)
-  // dQ^T work split: (head-dim tile, row tile) pairs spread over the 4 waves
-  constexpr int QCT = NCT == 4 ? 1 : 1;            // head-dim tiles per wave
-  constexpr int QNT = NCT == 4 ? 2 : 1;            // row tiles per wave
+  constexpr int CPT = DCH / 8;   // chunks per thread per staged matrix (8 threads per row)
+  constexpr int LDP = TR + 8;    // P^T / dS^T row stride (bf16)
   __shared__ __attribute__((aligned(16))) bf16raw Qs[2][TR * D];
   __shared__ __attribute__((aligned(16))) bf16raw dOs[2][TR * D];
   __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
-  __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
-  __shared__ __attribute__((aligned(16))) bf16raw dSt[BLK * LDT];
+  __shared__ __attribute__((aligned(16))) bf16raw PT[BLK * LDP];
+  __shared__ __attribute__((aligned(16))) bf16raw dST[BLK * LDP];
   __shared__ __attribute__((aligned(16))) float rlse[2][TR];
   __shared__ __attribute__((aligned(16))) float rdd[2][TR];
   __shared__ __attribute__((aligned(16))) int rlim[2][TR];
@@ -67,26 +66,31 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const int l32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
+  const int kq = wave & 3, hf = wave >> 2;
   const size_t kv0 = (size_t)(b * T + blk * BLK) * G + g;
   const size_t pair0 = (size_t)bg * W * K;
   const int32_t* lst = list + pair0 + start;
-  const int kw = 32 * wave;  // first key owned by this wave
+  const int kown = 32 * kq + l32;  // this lane's key (B column of S, M row of dK/dV)
   const int ntiles = (len + TT - 1) / TT;
 
-  // ---- K and V blocks -> LDS (swizzled row-major)
-  for (int c = tid; c < BLK * DCH; c += 256) {
+  // ---- K block -> LDS (swizzled row-major); own-key V rows -> registers
+  for (int c = tid; c < BLK * DCH; c += BWD_THREADS) {
     const int r = c / DCH, cc = c % DCH;
-    const size_t src = (kv0 + (size_t)r * G) * D + 8 * cc;
-    st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], ld16u(k + src));
-    st16u(&Vs[r * D + 8 * swz<DCH>(r, cc)], ld16u(v + src));
+    st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], ld16u(k + (kv0 + (size_t)r * G) * D + 8 * cc));
   }
-  f32x16 dka[NCT], dva[NCT];
+  bf16x8 bv[KSD];
+  {
+    const bf16raw* vr = v + (kv0 + (size_t)kown * G) * D + 8 * h;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) dka[ct] = dva[ct] = zero16();
+    for (int ks = 0; ks < KSD; ++ks) bv[ks] = ld8(vr + 16 * ks);
+  }
+  f32x16 dka[HCT], dva[HCT];
+#pragma unroll
+  for (int c = 0; c < HCT; ++c) dka[c] = dva[c] = zero16();
 
-  // ---- staging of one tile: thread tid owns row tid/4 and chunks (tid%4) + 4u
-  const int srow = tid >> 2, ssub = tid & 3;
+  // ---- staging of one tile: thread tid owns row tid/8 and chunks (tid%8) + 8u
+  const int srow = tid >> 3, ssub = tid & 7;
   uint4 sq[CPT], sdo[CPT];
   int s_pair = -1, s_lim = -1;
   float s_lse = INFINITY, s_dd = 0.f;
@@ -99,8 +103,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      sq[u] = val ? ld16u(q + hrow * D + 8 * (ssub + 4 * u)) : z;
-      sdo[u] = val ? ld16u(dout + hrow * D + 8 * (ssub + 4 * u)) : z;
+      sq[u] = val ? ld16u(q + hrow * D + 8 * (ssub + 8 * u)) : z;
+      sdo[u] = val ? ld16u(dout + hrow * D + 8 * (ssub + 8 * u)) : z;
     }
     s_lim = val ? t - blk * BLK : -1;
     s_lse = (val && ssub == 0) ? lse[hrow] * LOG2E : INFINITY;
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int off = srow * D + 8 * swz<DCH>(srow, ssub + 4 * u);
+      const int off = srow * D + 8 * swz<DCH>(srow, ssub + 8 * u);
       st16u(&Qs[buf][off], sq[u]);
       st16u(&dOs[buf][off], sdo[u]);
     }
@@ -128,134 +132,114 @@ __global__ __launch_bounds__(256, 1) void k_bwd_kv(
   }
   __syncthreads();
 
-  const int kown = kw + l32;
-  const int cw = NCT == 4 ? wave : (wave & 1);
-  const int nt0 = NCT == 4 ? 0 : (wave >> 1);
-  // A operands of dQ^T = K^T dS^T for this wave's head-dim slice, all 128 keys (8 k-steps)
-  bf16x8 akt[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int kr = 16 * ks + 8 * h + (i16 >> 2);
-    const int col = 32 * cw + 16 * (g16 & 1) + 4 * (i16 & 3);
-    const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
-    const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
-    akt[ks] = as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-  }
+  // dQ unit of this wave: head-dim tile qc, row tile qr (d = 64 has 4 units for 8 waves)
+  constexpr int QUNITS = NCT * 2;
+  const int qc = wave % NCT, qr = (wave / NCT) & 1;
+  const bool do_dq = wave < QUNITS;
+
   for (int ti = 0; ti < ntiles; ++ti) {
     const int cur = ti & 1;
     const bf16raw* Qc = Qs[cur];
     const bf16raw* dOc = dOs[cur];
-    uint2 dsw[2][4];  // dS as bf16 pairs, kept for the LDS exchange
 
-    bf16x8 bk[KSD], bv[KSD];  // own-key K/V operands, shared by both row tiles
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const int ko = kown * D + 8 * swz<DCH>(kown, 2 * ks + h);
-      bk[ks] = ld8(&Ks[ko]);
-      bv[ks] = ld8(&Vs[ko]);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      // ---- S = Q K^T, dP = dO V^T : 32 rows x the wave's 32 keys
-      f32x16 sacc = zero16(), pacc = zero16();
+    // ---- S = Q K^T, dP = dO V^T : rows 32hf.., the wave's 32 keys
+    f32x16 sacc = zero16(), pacc = zero16();
+    {
+      const int r = 32 * hf + l32;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
-        const int r = 32 * rt + l32;
+        const bf16x8 bk = ld8(&Ks[kown * D + 8 * swz<DCH>(kown, 2 * ks + h)]);
         const int off = r * D + 8 * swz<DCH>(r, 2 * ks + h);
-        sacc = mfma32(ld8(&Qc[off]), bk[ks], sacc);
+        sacc = mfma32(ld8(&Qc[off]), bk, sacc);
         pacc = mfma32(ld8(&dOc[off]), bv[ks], pacc);
       }
-      // ---- P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D): the
-      // softmax scale of both dK and dQ is folded in here; branch-free
+    }
+    // ---- P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D); lane
+    // holds key kown and rows 32hf + 8j + 4h + i
+    uint2 pw[4], dw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = 32 * rt + 8 * j + 4 * h;
-        const float4 lv = *reinterpret_cast<const float4*>(&rlse[cur][r0]);
-        const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[cur][r0]);
-        const int4 lm = *reinterpret_cast<const int4*>(&rlim[cur][r0]);
-        const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-        const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = 32 * hf + 8 * j + 4 * h;
+      const float4 lv = *reinterpret_cast<const float4*>(&rlse[cur][r0]);
+      const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[cur][r0]);
+      const int4 lm = *reinterpret_cast<const int4*>(&rlim[cur][r0]);
+      const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+      const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
+      float pv[4], dsv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * j + i;
-          const float ex = fast_exp2(sacc[e] * sl2 - la[i]);
-          const float pv = kown <= ma[i] ? ex : 0.f;
-          sacc[e] = pv;
-          pacc[e] = pv * fmaf(pacc[e], scale, -da[i]);
-        }
-        dsw[rt][j] = make_uint2(pack2(pacc[4 * j], pacc[4 * j + 1]), pack2(pacc[4 * j + 2], pacc[4 * j + 3]));
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * j + i;
+        const float ex = fast_exp2(sacc[e] * sl2 - la[i]);
+        pv[i] = kown <= ma[i] ? ex : 0.f;
+        dsv[i] = pv[i] * fmaf(pacc[e], scale, -da[i]);
       }
-      // ---- dV += P^T dO, dK += dS^T Q for the two 16-row K steps of this row tile
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const bf16x8 ap = as_bf8(make_uint4(
-            pack2(sacc[8 * ss + 0], sacc[8 * ss + 1]), pack2(sacc[8 * ss + 2], sacc[8 * ss + 3]),
-            pack2(sacc[8 * ss + 4], sacc[8 * ss + 5]), pack2(sacc[8 * ss + 6], sacc[8 * ss + 7])));
-        const bf16x8 ad = as_bf8(make_uint4(dsw[rt][2 * ss].x, dsw[rt][2 * ss].y, dsw[rt][2 * ss + 1].x,
-                                            dsw[rt][2 * ss + 1].y));
-        const int ra = 32 * rt + 16 * ss + 4 * h + (i16 >> 2);  // rows of the first transpose read
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const int col = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
-          const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
-          const int ob = (ra + 8) * D + 8 * swz<DCH>(ra + 8, col >> 3) + (col & 7);
-          const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
-          const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
-          dva[ct] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[ct]);
-          dka[ct] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[ct]);
-        }
-      }
+      pw[j] = make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]));
+      dw[j] = make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3]));
     }
 
-    __syncthreads();  // every wave is past the previous tile's dQ (dSt, rpair)
-    // ---- dS^T -> LDS [key][row]: lane holds key kown, rows 32rt + 8j + 4h + (0..3)
+    __syncthreads();  // X: previous tile's P^T/dS^T, Q/dO[cur^1] and row data are no longer read
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint2*>(&dSt[kown * LDT + 32 * rt + 8 * j + 4 * h]) = dsw[rt][j];
+    for (int j = 0; j < 4; ++j) {
+      const int o = kown * LDP + 32 * hf + 8 * j + 4 * h;
+      *reinterpret_cast<uint2*>(&PT[o]) = pw[j];
+      *reinterpret_cast<uint2*>(&dST[o]) = dw[j];
+    }
     stage_store(cur ^ 1);  // tile ti+1 (zeros past the list)
-    __syncthreads();       // dSt and the next tile are in LDS
+    __syncthreads();       // Y: P^T, dS^T and the next tile are in LDS
     stage_load(ti + 2);
 
-    // ---- dQ^T slice = K^T dS^T : head dim along M, rows along N, keys as K (8 steps)
-    f32x16 dq[QNT];
+    // ---- dV += P^T dO, dK += dS^T Q : own keys x head-dim tiles hf*HCT.., all 64 rows
 #pragma unroll
-    for (int n = 0; n < QNT; ++n) dq[n] = zero16();
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 ap = ld8(&PT[kown * LDP + 16 * st + 8 * h]);
+      const bf16x8 ad = ld8(&dST[kown * LDP + 16 * st + 8 * h]);
+      const int ra = 16 * st + 8 * h + (i16 >> 2);  // rows of the first transpose read
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int kr = 16 * ks + 8 * h + (i16 >> 2);
-#pragma unroll
-      for (int n = 0; n < QNT; ++n) {
-        const int rc = 32 * (nt0 + n) + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const uint2 b0 = lds_tr4(&dSt[kr * LDT + rc]);
-        const uint2 b1 = lds_tr4(&dSt[(kr + 4) * LDT + rc]);
-        dq[n] = mfma32(akt[ks], as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq[n]);
+      for (int c = 0; c < HCT; ++c) {
+        const int col = 32 * (hf * HCT + c) + 16 * g16 + 4 * (i16 & 3);
+        const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
+        const int ob = (ra + 4) * D + 8 * swz<DCH>(ra + 4, col >> 3) + (col & 7);
+        const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
+        const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
+        dva[c] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[c]);
+        dka[c] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[c]);
       }
     }
-    // lane holds row 32(nt0+n) + l32, head-dim columns 32cw + 8j + 4h + (0..3)
+
+    // ---- dQ^T tile = K^T dS^T : head-dim tile qc along M, row tile qr along N, keys as K
+    if (do_dq) {
+      f32x16 dq = zero16();
 #pragma unroll
-    for (int n = 0; n < QNT; ++n) {
-      const int row = 32 * (nt0 + n) + l32;
+      for (int ks = 0; ks < 8; ++ks) {
+        const int kr = 16 * ks + 8 * h + (i16 >> 2);
+        const int col = 32 * qc + 16 * g16 + 4 * (i16 & 3);
+        const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
+        const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
+        const int rc = 32 * qr + 16 * g16 + 4 * (i16 & 3);
+        const uint2 b0 = lds_tr4(&dST[kr * LDP + rc]);
+        const uint2 b1 = lds_tr4(&dST[(kr + 4) * LDP + rc]);
+        dq = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq);
+      }
+      // lane holds row 32qr + l32, head-dim columns 32qc + 8j + 4h + (0..3)
+      const int row = 32 * qr + l32;
       const int p = rpair[cur][row];
       if (p >= 0) {
-        bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * cw + 4 * h;
+        bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * qc + 4 * h;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          st4bf(dst + 8 * j, dq[n][4 * j], dq[n][4 * j + 1], dq[n][4 * j + 2], dq[n][4 * j + 3]);
+        for (int j = 0; j < 4; ++j) st4bf(dst + 8 * j, dq[4 * j], dq[4 * j + 1], dq[4 * j + 2], dq[4 * j + 3]);
       }
     }
   }
 
-  // ---- dK, dV of the owned keys: lane holds head-dim column 32ct + l32, keys kw + 8j + 4h + i
+  // ---- dK, dV of the owned keys: lane holds head-dim column 32ct + l32, keys 32kq + 8j + 4h + i
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int c = 0; c < HCT; ++c)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int kk = kw + 8 * (e >> 2) + 4 * h + (e & 3);
-      const size_t off = (kv0 + (size_t)kk * G) * D + 32 * ct + l32;
-      dk_acc[off] += dka[ct][e];
-      dv_acc[off] += dva[ct][e];
+      const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
+      const size_t off = (kv0 + (size_t)kk * G) * D + 32 * (hf * HCT + c) + l32;
+      dk_acc[off] += dka[c][e];
+      dv_acc[off] += dva[c][e];
     }
 }
 
@@ -344,7 +328,7 @@ template <int D, int R>
 static hipError_t bwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* dout, const float* lse, const float* Dd, const InvBufs& ib,
                                  uint16_t* dq_part, float* dk_acc, float* dv_acc, hipStream_t st) {
-  dim3 grid(ib.max_items, g.B * g.G), block(256);
+  dim3 grid(ib.max_items, g.B * g.G), block(BWD_THREADS);
   k_bwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, dout, lse, Dd, ib.items, ib.item_count, ib.list, dq_part, dk_acc,
                                          dv_acc, g.T, g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale,
                                          g.scale * LOG2E);
