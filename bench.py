@@ -39,6 +39,89 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "MSA fwd+bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), 128K & 1M"
 
+# Library timing slot -> kernel symbol prefix and the source file it is built from.
+KERNELS = {
+    "proxy_pool": ("k_proxy_pool<", "msa_select.hip"),
+    "topk": ("k_topk<", "msa_select.hip"),
+    "inverse": ("k_inv_scatter", "msa_inverse.hip"),
+    "fwd_partials": ("k_fwd_kv<", "msa_fwd.hip"),
+    "fwd_combine": ("k_fwd_combine<", "msa_fwd.hip"),
+    "bwd_dot": ("k_bwd_dot<", "msa_bwd.hip"),
+    "bwd_partials": ("k_bwd_kv<", "msa_bwd.hip"),
+    "dq_combine": ("k_dq_combine<", "msa_bwd.hip"),
+    "convert": ("k_cvt_bf16", "msa_bwd.hip"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msa_hbm_traffic_128k.md")
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of what a kernel is compiled from (its source, the shared headers and
+    the build flags): stored HBM counter figures apply only while it matches."""
+    import hashlib
+    csrc = os.path.join(ROOT, "block_sparse_attention_qk_amd", "csrc")
+    h = hashlib.sha256()
+    for path in (os.path.join(csrc, KERNELS[name][1]), os.path.join(csrc, "msa_common.h"),
+                 os.path.join(csrc, "msa_internal.h"), os.path.join(ROOT, "block_sparse_attention_qk_amd", "build.py")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, name: str):
+    """Calibrated HBM bytes per launch (read + write) of one kernel, from the
+    committed counter summary, or None if absent or taken on other code."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        f = dict(kv.split("=", 1) for kv in line.split()[1:] if "=" in kv) if line.startswith("traffic ") else {}
+        if f.get("workload") == workload and f.get("kernel") == name:
+            if f.get("source") != kernel_source_hash(name):
+                return None
+            return int(f["read_bytes"]) + int(f["write_bytes"])
+    return None
+
+
+def pmc_summary(pmc_dir: str, copy_mib: int, workload: str) -> str:
+    """Per-kernel HBM bytes per dispatch from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain device copy of copy_mib MiB in the same run."""
+    import csv
+    import glob
+    vals = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = {}
+        for f in glob.glob(os.path.join(pmc_dir, ctr, "*_counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == ctr:
+                    per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        vals[ctr] = per
+    copy_bytes = float(copy_mib << 20)
+    factor = {}
+    for ctr in vals:
+        cands = [max(v) for k, v in vals[ctr].items() if "copyBuffer" in k]
+        if not cands:
+            raise SystemExit("no copy kernel in the %s run" % ctr)
+        factor[ctr] = copy_bytes / max(cands)
+    out = ["Copy calibration (%d MiB device copy): FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (
+        copy_mib, factor["FETCH_SIZE"], factor["WRITE_SIZE"]), "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GiB | write GiB |", "|---|---|---|---|---|---|"]
+    lines = []
+    for name, (sym, _) in KERNELS.items():
+        rd = [v for k, v in vals["FETCH_SIZE"].items() if sym in k]
+        wr = [v for k, v in vals["WRITE_SIZE"].items() if sym in k]
+        if not rd or not wr:
+            continue
+        rd = [x for v in rd for x in v]
+        wr = [x for v in wr for x in v]
+        r_avg, w_avg = sum(rd) / len(rd), sum(wr) / len(wr)
+        rb, wb = r_avg * factor["FETCH_SIZE"], w_avg * factor["WRITE_SIZE"]
+        out.append("| %s (%s) | %d | %.0f | %.0f | %.3f | %.3f |" % (
+            name, sym.rstrip("<"), len(rd), r_avg / 1024, w_avg / 1024, rb / 2**30, wb / 2**30))
+        lines.append("traffic workload=%s kernel=%s read_bytes=%d write_bytes=%d source=%s" % (
+            workload, name, rb, wb, kernel_source_hash(name)))
+    return "\n".join(out + ["", "```"] + lines + ["```"])
+
+
 
 def gpu_inputs(cfg: synth.Config, seed: int = 0) -> dict:
     """Same recipe as synth (N(0,1) bf16; proxy keys plus a per-block mean of
@@ -164,7 +247,7 @@ def roofline(cfg: synth.Config, kern: dict, steps: int) -> dict:
     else:
         achieved, peak = work / avg_s / 1e9, PEAK_HBM_GBS
     return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": None, "avg_launch_ms": avg_s * 1e3,
+            "frac": achieved / peak, "traffic": stored_traffic(cfg.name, name), "avg_launch_ms": avg_s * 1e3,
             "work_per_launch": work}
 
 
@@ -216,7 +299,13 @@ def main() -> int:
                     help="also run one plain device copy of this many MiB (reference kernel for traffic counters)")
     ap.add_argument("--gpu-inputs", action="store_true",
                     help="draw the main workload's inputs on the GPU (same recipe, different stream; for profiling)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="print calibrated per-kernel HBM bytes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
+                         "(needs --copy-calibration-mib of those runs) and exit; no GPU needed")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.copy_calibration_mib or 1024, args.config))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
               file=sys.stderr)

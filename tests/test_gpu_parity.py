@@ -186,3 +186,70 @@ def test_16k_config_sampled(msa, oracle_mod):
 def test_128k_config_sampled(msa, oracle_mod):
     cfg = synth.CONFIGS["128k"]
     _sampled_check(msa, oracle_mod, cfg, n_rows=512, blocks_per_group=[cfg.N // 2, cfg.N - 3, cfg.N - 1])
+
+
+def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
+    """Full-size run with inputs drawn on the GPU (same recipe as synth: N(0,1)
+    bf16, block-mean proxy keys), checked on sampled rows and on late key
+    blocks.  The oracle gets full-size host arrays in which only the rows it
+    reads are filled (the rest stay untouched zero pages)."""
+    import bench
+    print("gpu-generated case", cfg, flush=True)
+    x = bench.gpu_inputs(cfg, seed=seed)
+    idx_d = msa.msa_proxy_select(x["qp"], x["kp"], cfg.topk)
+    o, lse = msa.msa_fwd(x["q"], x["k"], x["v"], idx_d)
+    dq, dk, dv = msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx_d)
+    torch.cuda.synchronize()
+    dm = _dims(cfg)
+    N, R = cfg.N, cfg.H // cfg.G
+    rng = np.random.default_rng(4321)
+    rows = np.sort(rng.choice(cfg.B * cfg.T, size=n_rows, replace=False))
+    bt, tt = torch.from_numpy(rows // cfg.T), torch.from_numpy(rows % cfg.T)
+    idx = idx_d.cpu().numpy()
+    # tokens whose rows the oracle reads: the samples and every selector of the checked blocks
+    blocks = [N - 1 - i for i in blocks_from_end]
+    sel = np.zeros(cfg.T, dtype=bool)
+    sel[rows % cfg.T] = True
+    for g in range(cfg.G):
+        for blk in blocks:
+            sel |= (idx[0, g] == blk).any(axis=1)
+    need = torch.from_numpy(np.nonzero(sel)[0])
+    print("oracle rows", int(need.numel()), flush=True)
+
+    def host_rows(t):
+        full = np.zeros(tuple(t.shape), dtype=np.float64)
+        full[0, need.numpy()] = t[0, need.cuda()].double().cpu().numpy()
+        return full
+
+    qp64 = np.zeros(tuple(x["qp"].shape), dtype=np.float64)
+    qp64[0, rows % cfg.T] = x["qp"][0, tt.cuda()].double().cpu().numpy()
+    kp64 = x["kp"].double().cpu().numpy()
+    idx_ref, pooled = oracle_mod.select(dm, qp64, kp64, rows=rows, return_pooled=True)
+    del kp64, qp64
+    info = parity.check_indices(idx[0][:, rows % cfg.T, :].transpose(1, 0, 2), idx_ref, pooled, cfg.topk)
+    print("indices", info, flush=True)
+    q64, do64 = host_rows(x["q"]), host_rows(x["dout"])
+    k64, v64 = x["k"].double().cpu().numpy(), x["v"].double().cpu().numpy()
+    o_ref, lse_ref = oracle_mod.fwd(dm, q64, k64, v64, idx, rows=rows)
+    res = [parity.assert_close("o", o[bt.cuda(), tt.cuda()].cpu(), o_ref, COS),
+           parity.assert_close("lse", lse[bt.cuda(), tt.cuda()].cpu(), lse_ref, COS)]
+    dq_ref = oracle_mod.bwd_rows(dm, q64, k64, v64, do64, idx, rows=rows)
+    res.append(parity.assert_close("dq", dq[bt.cuda(), tt.cuda()].cpu(), dq_ref, COS))
+    codes = [g * N + blk for g in range(cfg.G) for blk in blocks]
+    dk_ref, dv_ref = oracle_mod.bwd_blocks(dm, q64, k64, v64, do64, idx, codes)
+    dk_g = torch.stack([dk[0, (c % N) * 128:(c % N) * 128 + 128, c // N].cpu() for c in codes])
+    dv_g = torch.stack([dv[0, (c % N) * 128:(c % N) * 128 + 128, c // N].cpu() for c in codes])
+    res.append(parity.assert_close("dk_blocks", dk_g, dk_ref, COS))
+    res.append(parity.assert_close("dv_blocks", dv_g, dv_ref, COS))
+    dv_sum = dv.double().sum(dim=1)
+    do_sum = x["dout"].double().view(cfg.B, cfg.T, cfg.G, R, cfg.d).sum(dim=(1, 3))
+    parity.assert_close("dv_total", dv_sum.cpu(), do_sum.cpu(), 0.99999, 1e-3 * do_sum.abs().max().item())
+    print(res, flush=True)
+
+
+def test_512k_config_gpu_generated(msa, oracle_mod):
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["512k"], n_rows=256, blocks_from_end=[0, 2])
+
+
+def test_1m_config_gpu_generated(msa, oracle_mod):
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=128, blocks_from_end=[0, 1])
