@@ -59,8 +59,8 @@ Layout layout(const Geo& g, msa_op op, int W) {
     L.pooled = c.take(BG * (size_t)W * g.N * 4);
   } else if (op == MSA_OP_FWD) {
     carve_inverse(L, c, g, W, FWD_ITEM_TOKENS);
-    L.part_o = c.take(pairs * g.R * g.D * 2);
-    L.part_lse = c.take(pairs * g.R * 4);
+    L.part_o = c.take((pairs + 1) * g.R * g.D * 2);  // + a spare slot for rows past an item's list
+    L.part_lse = c.take((pairs + 1) * g.R * 4);
   } else {
     const size_t kv = (size_t)g.B * g.T * g.G * g.D;
     L.Dd = c.take((size_t)g.B * g.T * g.H * 4);

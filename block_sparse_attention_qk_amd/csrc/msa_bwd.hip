@@ -60,9 +60,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) int rlim[2][TR];
   __shared__ __attribute__((aligned(16))) int rpair[2][TR];
 
-  const int bg = blockIdx.y;
-  if ((int)blockIdx.x >= item_count[bg]) return;
-  const int4 it = items[(size_t)bg * max_items + blockIdx.x];
+  // Groups interleave in dispatch order (bg fastest) so that each group's
+  // long early-block items start near the beginning of the launch.
+  const int BG = (int)gridDim.x / max_items;
+  const int bg = (int)blockIdx.x % BG, item = (int)blockIdx.x / BG;
+  if (item >= item_count[bg]) return;
+  const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -75,9 +78,19 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
   const int ntiles = (len + TT - 1) / TT;
 
   // ---- K block -> LDS (swizzled row-major); own-key V rows -> registers
-  for (int c = tid; c < BLK * DCH; c += BWD_THREADS) {
-    const int r = c / DCH, cc = c % DCH;
-    st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], ld16u(k + (kv0 + (size_t)r * G) * D + 8 * cc));
+  {
+    constexpr int NLD = BLK * DCH / BWD_THREADS;  // 16-byte chunks per thread
+    uint4 kr[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {  // all loads first, then all LDS stores
+      const int c = tid + BWD_THREADS * u;
+      kr[u] = ld16u(k + (kv0 + (size_t)(c / DCH) * G) * D + 8 * (c % DCH));
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int c = tid + BWD_THREADS * u, r = c / DCH, cc = c % DCH;
+      st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], kr[u]);
+    }
   }
   bf16x8 bv[KSD];
   {
@@ -89,26 +102,29 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
 #pragma unroll
   for (int c = 0; c < HCT; ++c) dka[c] = dva[c] = zero16();
 
-  // ---- staging of one tile: thread tid owns row tid/8 and chunks (tid%8) + 8u
+  // ---- staging of one tile: thread tid owns row tid/8 and chunks (tid%8) + 8u.
+  // Loads never branch and never wait where they are issued: a row past the
+  // list reads the list's last entry (finite data, masked at store time), the
+  // list entry of tile i+2 is fetched at the top of iteration i (no loaded
+  // value is carried across iterations), and scaling and validity are applied
+  // when the staged registers go to LDS, a full tile later.
   const int srow = tid >> 3, ssub = tid & 7;
   uint4 sq[CPT], sdo[CPT];
-  int s_pair = -1, s_lim = -1;
-  float s_lse = INFINITY, s_dd = 0.f;
-  auto stage_load = [&](int ti) {
-    const int li = ti * TT + srow / R;
-    const bool val = li < len;
-    s_pair = val ? lst[li] : -1;
-    const int t = val ? t0 + s_pair / K : 0;
+  int s_li = len, s_pair = 0;
+  float s_lse = 0.f, s_dd = 0.f;
+  auto list_entry = [&](int ti) { return lst[min(ti * TT + srow / R, len - 1)]; };
+  auto stage_load = [&](int ti, int pair) {
+    s_li = ti * TT + srow / R;
+    s_pair = pair;
+    const int t = t0 + pair / K;
     const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      sq[u] = val ? ld16u(q + hrow * D + 8 * (ssub + 8 * u)) : z;
-      sdo[u] = val ? ld16u(dout + hrow * D + 8 * (ssub + 8 * u)) : z;
+      sq[u] = ld16u(q + hrow * D + 8 * (ssub + 8 * u));
+      sdo[u] = ld16u(dout + hrow * D + 8 * (ssub + 8 * u));
     }
-    s_lim = val ? t - blk * BLK : -1;
-    s_lse = (val && ssub == 0) ? lse[hrow] * LOG2E : INFINITY;
-    s_dd = (val && ssub == 0) ? Dd[hrow] * scale : 0.f;
+    s_lse = lse[hrow];
+    s_dd = Dd[hrow];
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
@@ -118,18 +134,24 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
       st16u(&dOs[buf][off], sdo[u]);
     }
     if (ssub == 0) {
-      rlse[buf][srow] = s_lse;
-      rdd[buf][srow] = s_dd;
-      rlim[buf][srow] = s_lim;
-      rpair[buf][srow] = s_pair;
+      const bool val = s_li < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
+      rlse[buf][srow] = val ? s_lse * LOG2E : INFINITY;
+      rdd[buf][srow] = s_dd * scale;
+      rlim[buf][srow] = val ? t0 + s_pair / K - blk * BLK : -1;
+      rpair[buf][srow] = val ? s_pair : -1;
     }
   };
 
   if (ntiles > 0) {
-    stage_load(0);
+    stage_load(0, list_entry(0));
     stage_store(0);
-    stage_load(1);  // rows past the list load as zeros
   }
+  // All prologue loads (the V operand included) complete here, so that the
+  // loop's V operand uses carry no wait on later loads.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+#pragma unroll
+  for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bv[ks]));  // operand now defined by a non-memory op
+  if (ntiles > 0) stage_load(1, list_entry(1));
   __syncthreads();
 
   // dQ unit of this wave: head-dim tile qc, row tile qr (d = 64 has 4 units for 8 waves)
@@ -141,6 +163,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
     const int cur = ti & 1;
     const bf16raw* Qc = Qs[cur];
     const bf16raw* dOc = dOs[cur];
+    const int pair2 = list_entry(ti + 2);  // consumed after barrier Y
 
     // ---- S = Q K^T, dP = dO V^T : rows 32hf.., the wave's 32 keys
     f32x16 sacc = zero16(), pacc = zero16();
@@ -186,7 +209,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
     }
     stage_store(cur ^ 1);  // tile ti+1 (zeros past the list)
     __syncthreads();       // Y: P^T, dS^T and the next tile are in LDS
-    stage_load(ti + 2);
+    stage_load(ti + 2, pair2);
 
     // ---- dV += P^T dO, dK += dS^T Q : own keys x head-dim tiles hf*HCT.., all 64 rows
 #pragma unroll
@@ -328,7 +351,8 @@ template <int D, int R>
 static hipError_t bwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* dout, const float* lse, const float* Dd, const InvBufs& ib,
                                  uint16_t* dq_part, float* dk_acc, float* dv_acc, hipStream_t st) {
-  dim3 grid(ib.max_items, g.B * g.G), block(BWD_THREADS);
+  if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid(ib.max_items * g.B * g.G), block(BWD_THREADS);
   k_bwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, dout, lse, Dd, ib.items, ib.item_count, ib.list, dq_part, dk_acc,
                                          dv_acc, g.T, g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale,
                                          g.scale * LOG2E);

@@ -43,9 +43,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
   __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
 
-  const int bg = blockIdx.y;
-  if ((int)blockIdx.x >= item_count[bg]) return;
-  const int4 it = items[(size_t)bg * max_items + blockIdx.x];
+  // Groups interleave in dispatch order (bg fastest) so that each group's
+  // long early-block items start near the beginning of the launch.
+  const int BG = (int)gridDim.x / max_items;
+  const int bg = (int)blockIdx.x % BG, item = (int)blockIdx.x / BG;
+  if (item >= item_count[bg]) return;
+  const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -54,34 +57,55 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   const size_t pair0 = (size_t)bg * W * K;
   const int32_t* lst = list + pair0 + start;
 
-  for (int c = tid; c < BLK * DCH; c += 256) {
-    const int r = c / DCH, cc = c % DCH;
-    const size_t src = (kv0 + (size_t)r * G) * D + 8 * cc;
-    st16u(&Ks[r * D + 8 * fswz<DCH>(r, cc)], ld16u(k + src));
-    st16u(&Vs[r * D + 8 * fswz<DCH>(r, cc)], ld16u(v + src));
+  {
+    constexpr int NLD = BLK * DCH / 256;  // 16-byte chunks per thread and matrix
+    uint4 kr[NLD], vr[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {  // all loads first, then all LDS stores
+      const int c = tid + 256 * u, r = c / DCH, cc = c % DCH;
+      const size_t src = (kv0 + (size_t)r * G) * D + 8 * cc;
+      kr[u] = ld16u(k + src);
+      vr[u] = ld16u(v + src);
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int c = tid + 256 * u, r = c / DCH, cc = c % DCH;
+      st16u(&Ks[r * D + 8 * fswz<DCH>(r, cc)], kr[u]);
+      st16u(&Vs[r * D + 8 * fswz<DCH>(r, cc)], vr[u]);
+    }
   }
 
-  // this lane's query row within a tile and its Q operand (B of S^T: column = row)
+  // this lane's query row within a tile and its Q operand (B of S^T: column = row).
+  // Loads never branch: a row past the list reads the list's last entry
+  // (finite data; its result is dropped).  The list entry of tile i+1 is
+  // fetched at the top of iteration i and used after the softmax, so the row
+  // address does not wait on memory and no loaded value crosses iterations.
   const int row = 32 * wave + l32;
   const int tt = row / R, hh = row % R;
-  auto load_q = [&](int ti, bf16x8* bq, int& pr, int& lim) {
-    const int li = ti * TT + tt;
-    const bool val = li < len;
-    pr = val ? lst[li] : -1;
-    const int t = val ? t0 + pr / K : 0;
+  auto list_entry = [&](int ti) { return lst[min(ti * TT + tt, len - 1)]; };
+  auto load_q = [&](int ti, int pair, bf16x8* bq, int& pr, int& lim) {
+    const bool val = ti * TT + tt < len;
+    const int t = t0 + pair / K;
+    pr = val ? pair : -1;
     lim = val ? t - blk * BLK : BLK - 1;
     const bf16raw* qr = q + ((size_t)(b * T + t) * H + g * R + hh) * D + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) bq[ks] = val ? ld8(qr + 16 * ks) : zero8();
+    for (int ks = 0; ks < KSD; ++ks) bq[ks] = ld8(qr + 16 * ks);
   };
 
   const int ntiles = (len + TT - 1) / TT;
   bf16x8 bq[KSD];
   int pr = -1, lim = BLK - 1;
-  if (ntiles > 0) load_q(0, bq, pr, lim);
+  if (ntiles > 0) load_q(0, list_entry(0), bq, pr, lim);
+  // The prologue's loads complete here and the first Q operand is redefined
+  // by a non-memory op, so that the loop's waits count only its own traffic.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+#pragma unroll
+  for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bq[ks]));
   __syncthreads();
 
   for (int ti = 0; ti < ntiles; ++ti) {
+    const int pair1 = list_entry(ti + 1);  // consumed after the softmax
     // S^T = K Q^T: 4 key tiles of 32 along M, this wave's 32 rows along N
     f32x16 acc[4];
 #pragma unroll
@@ -131,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
           pack2(acc[kt][8 * ss + 4], acc[kt][8 * ss + 5]), pack2(acc[kt][8 * ss + 6], acc[kt][8 * ss + 7])));
     }
 
-    if (ti + 1 < ntiles) load_q(ti + 1, bq, pr, lim);  // next tile's rows in flight during PV
+    load_q(ti + 1, pair1, bq, pr, lim);  // next tile's rows in flight during PV (past the end: unused)
 
     // O^T = V^T P^T: head dim along M (NCT tiles), rows along N, keys as K (8 steps of 16)
     f32x16 oacc[NCT];
@@ -151,9 +175,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
     }
 
     // lane holds row `row`, head-dim columns 32ct + 8j + 4h + (0..3)
-    if (cpr >= 0) {
+    // Stores never branch (so the next tile's loads are waited on alone): a
+    // row past the list writes the spare slot after the window's pairs.
+    {
       const float inv = 1.0f / l;
-      const size_t pidx = pair0 + (size_t)cpr;
+      const size_t pidx = cpr >= 0 ? pair0 + (size_t)cpr : (size_t)BG * W * K;
       bf16raw* dst = part_o + (pidx * R + hh) * D + 4 * h;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -161,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
         for (int j = 0; j < 4; ++j)
           st4bf(dst + 32 * ct + 8 * j, oacc[ct][4 * j] * inv, oacc[ct][4 * j + 1] * inv, oacc[ct][4 * j + 2] * inv,
                 oacc[ct][4 * j + 3] * inv);
-      if (h == 0) part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;
+      part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;  // both lane halves hold the same value
     }
   }
 }
@@ -189,41 +215,43 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   const float* pl = part_lse + p0 * R + hh;
   const bf16raw* po = part_o + (p0 * R + hh) * D + c8;
 
+  // One pass with a running maximum: each batch loads its slots' lse and
+  // partial rows together, and the accumulator is rescaled when the maximum grows.
   constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
-  float M = -INFINITY;
+  float M = -INFINITY, L = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < K; s0 += SB) {
+    float lv[SB];
+    uint4 raw[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       const int s = s0 + u;
-      if (s < K && (unsigned)ir[s] <= last) M = fmaxf(M, pl[(size_t)s * R]);
+      const bool ok = s < K && (unsigned)ir[s] <= last;
+      lv[u] = ok ? pl[(size_t)s * R] : -INFINITY;
+      raw[u] = ok ? ld16u(po + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
     }
-  }
-  float L = 0.f, acc[8];
+    float mb = M;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (M != -INFINITY) {
-    const float Ml = M * LOG2E;
-    for (int s0 = 0; s0 < K; s0 += SB) {
-      float w[SB];
-      uint4 raw[SB];
+    for (int u = 0; u < SB; ++u) mb = fmaxf(mb, lv[u]);
+    if (mb == -INFINITY) continue;  // no valid slot yet
+    const float mbl = mb * LOG2E;
+    const float c = fast_exp2(M * LOG2E - mbl);  // 0 while M is still -inf
+    L *= c;
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const int s = s0 + u;
-        const bool ok = s < K && (unsigned)ir[s] <= last;
-        w[u] = ok ? fast_exp2(pl[(size_t)s * R] * LOG2E - Ml) : 0.f;
-        raw[u] = ok ? ld16u(po + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int i = 0; i < 8; ++i) acc[i] *= c;
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        L += w[u];
-        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    for (int u = 0; u < SB; ++u) {
+      const float w = fast_exp2(lv[u] * LOG2E - mbl);  // 0 for an invalid slot
+      L += w;
+      const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          acc[2 * m] += w[u] * __uint_as_float(wd[m] << 16);
-          acc[2 * m + 1] += w[u] * __uint_as_float(wd[m] & 0xffff0000u);
-        }
+      for (int m = 0; m < 4; ++m) {
+        acc[2 * m] += w * __uint_as_float(wd[m] << 16);
+        acc[2 * m + 1] += w * __uint_as_float(wd[m] & 0xffff0000u);
       }
     }
+    M = mb;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const size_t orow = (size_t)(b * T + t) * H + g * R + hh;
@@ -235,7 +263,8 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
 template <int D, int R>
 static hipError_t fwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const InvBufs& ib, uint16_t* part_o, float* part_lse, hipStream_t st) {
-  dim3 grid(ib.max_items, g.B * g.G), block(256);
+  if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid(ib.max_items * g.B * g.G), block(256);
   k_fwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, ib.items, ib.item_count, ib.list, part_o, part_lse, g.T, g.H,
                                          g.G, g.K, w.t0, w.W, ib.max_items, g.scale, g.scale * LOG2E);
   return hipGetLastError();
