@@ -6,121 +6,153 @@
 // training", paragraphs 1, 3, 4): one proxy head per KV group scores every
 // query against every causal key, scores are max-pooled over 128-key blocks,
 // and the top-k blocks per query are cached.  This is the only quadratic step.
+#include <type_traits>
+
 #include "msa_common.h"
 #include "msa_internal.h"
 
 namespace msa {
 
-constexpr int POOL_QT = 256;   // queries per workgroup (4 waves x 64)
-constexpr int POOL_CHB = 16;   // pooled blocks buffered in LDS between flushes
+constexpr int POOL_WAVES = 8;  // waves per workgroup, 32 queries each
+constexpr int POOL_QT = 32 * POOL_WAVES;  // queries per workgroup
+constexpr int POOL_CHB = 8;    // pooled blocks collected in LDS per flush
+constexpr int POOL_NBUF = 3;   // key-block ring in LDS (DMA two blocks ahead)
+
+// Position of 16-byte chunk c of key row r in a proxy key tile of DP dims:
+// rows of 2*DP bytes, 256/(2*DP) rows per LDS bank line; the XOR spreads 16
+// consecutive rows over all banks for 16-byte operand reads.
+template <int DP>
+__device__ __forceinline__ int kswz(int r, int c) {
+  constexpr int CPR = DP / 8, RPL = 128 / DP;
+  return c ^ ((r / RPL) & (CPR - 1));
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete,
+// then all waves meet.  Global-to-LDS copies still in flight are not waited
+// for (the caller waits for exactly the ones it needs).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Pooled scores for the queries [t0, t0+W) of one (batch, group):
 //   pooled[(bg*W + t - t0)*N + i] = max_{128i <= j <= min(128i+127, t)} qp[t].kp[j]
 // for i <= t/128 (other entries are not written).
 //
-// Each wave owns 64 queries (4 MFMA column tiles) whose proxy rows stay in
-// registers as B operands.  Key blocks stream through a double-buffered LDS
-// tile; the product is taken transposed (S^T = Kp Qp^T, keys along M) so that a
-// lane holds 32 keys of one query column: the block max is 31 in-lane maxima
-// and two cross-lane steps.  Pooled values collect in LDS and leave as 64-byte
-// row segments.
+// Each wave owns 32 queries (one MFMA column tile) whose proxy rows stay in
+// registers as B operands; small per-wave state keeps four waves per SIMD.  The product is taken transposed,
+// S^T = Kp Qp^T on v_mfma_f32_32x32x16_bf16 with keys along M, so that a lane
+// holds 16 keys of one query column per key tile: the block max is in-lane
+// maxima and one cross-lane step.  Key blocks arrive in a three-deep LDS ring
+// by global-to-LDS copies issued two blocks ahead; pooled values collect in a
+// double-buffered LDS table and leave as 32-byte row segments.
 template <int DP>
-__global__ __launch_bounds__(256, 2) void k_proxy_pool(const bf16raw* __restrict__ qp,
+__global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw* __restrict__ qp,
                                                        const bf16raw* __restrict__ kp,
                                                        float* __restrict__ pooled, int T, int G, int N,
                                                        int t0, int W) {
-  constexpr int KS = DP / 32;      // MFMA k-steps over the proxy dim
-  constexpr int LDK = DP + 8;      // LDS row stride in bf16 (keeps 16 rows on distinct banks)
-  constexpr int CPT = DP / 16;     // 16-byte chunks per thread per key block
-  __shared__ __attribute__((aligned(16))) bf16raw kbuf[2][BLK * LDK];
-  __shared__ float pbuf[POOL_QT * (POOL_CHB + 1)];
+  constexpr int KS = DP / 16;          // k-steps of 16 over the proxy dim
+  constexpr int CPR = DP / 8;          // 16-byte chunks per key row
+  constexpr int NDMA = BLK * CPR / (64 * POOL_WAVES);  // 1 KiB copies per wave per key block
+  constexpr int PST = POOL_CHB + 1;    // pooled table row stride (floats)
+  // three ring slots as separate arrays: with the slot of every access known at
+  // compile time, the copies into one slot are seen not to alias reads of another
+  __shared__ __attribute__((aligned(16))) bf16raw kslot0[BLK * DP];
+  __shared__ __attribute__((aligned(16))) bf16raw kslot1[BLK * DP];
+  __shared__ __attribute__((aligned(16))) bf16raw kslot2[BLK * DP];
+  __shared__ float pbuf[2][POOL_QT * PST];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, q4 = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
   const int bg = blockIdx.y, b = bg / G, g = bg % G;
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int qt0 = t0 + tile * POOL_QT;
   const int qlast = min(qt0 + POOL_QT, t0 + W) - 1;
   const int kb_last = qlast / BLK;
 
-  bf16x8 bq[4][KS];
-  int tq[4];
+  // B operands: query column 32*wave + l32, proxy dims 16ks + 8h .. +7
+  bf16x8 bq[KS];
+  const int tq = qt0 + 32 * wave + l32;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    tq[nt] = qt0 + 64 * wave + 16 * nt + l16;
-    const bool ok = tq[nt] <= qlast;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bq[nt][ks] = ok ? ld8(qp + ((size_t)(b * T + tq[nt]) * G + g) * DP + 32 * ks + 8 * q4) : zero8();
-  }
+  for (int ks = 0; ks < KS; ++ks)
+    bq[ks] = tq <= qlast ? ld8(qp + ((size_t)(b * T + tq) * G + g) * DP + 16 * ks + 8 * h) : zero8();
 
-  bf16x8 pre[CPT];
-  auto gload = [&](int kb) {
+  auto slot_ptr = [&](auto sl) -> bf16raw* {
+    if constexpr (decltype(sl)::value == 0) return kslot0;
+    else if constexpr (decltype(sl)::value == 1) return kslot1;
+    else return kslot2;
+  };
+  // Copy of key block kb (clamped to the last one) into a ring slot.  Lane l of
+  // copy u lands at slot byte 1024 (NDMA wave + u) + 16 l: key row r, physical
+  // chunk p; it fetches the logical chunk p ^ swizzle(r).
+  auto dma = [&](int kb, bf16raw* slot) {
+    const int kbc = min(kb, kb_last);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = threadIdx.x + 256 * u, r = c / (DP / 8), c8 = c % (DP / 8);
-      pre[u] = ld8(kp + ((size_t)(b * T + kb * BLK + r) * G + g) * DP + 8 * c8);
+    for (int u = 0; u < NDMA; ++u) {
+      const int cidx = (NDMA * wave + u) * 64 + lane, r = cidx / CPR, pch = cidx % CPR;
+      const bf16raw* src = kp + ((size_t)(b * T + kbc * BLK + r) * G + g) * DP + 8 * kswz<DP>(r, pch);
+      __builtin_amdgcn_global_load_lds(src, slot + (NDMA * wave + u) * 512, 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = threadIdx.x + 256 * u, r = c / (DP / 8), c8 = c % (DP / 8);
-      st8(&kbuf[buf][r * LDK + 8 * c8], pre[u]);
+  auto flush = [&](int chunk) {  // pooled blocks [chunk*8, chunk*8+8) of the 256 queries
+    const int kb0 = chunk * POOL_CHB;
+    const float* pb = pbuf[chunk & 1];
+    for (int i = threadIdx.x; i < POOL_QT * POOL_CHB; i += 64 * POOL_WAVES) {
+      const int r = i / POOL_CHB, c = i % POOL_CHB, t = qt0 + r;
+      if (kb0 + c <= kb_last && t <= qlast && kb0 + c <= t / BLK)
+        pooled[((size_t)bg * W + (t - t0)) * N + kb0 + c] = pb[r * PST + c];
     }
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kb = 0; kb <= kb_last; ++kb) {
-    const int cur = kb & 1;
-    if (kb < kb_last) gload(kb + 1);
+  // One key block: block kb is in slot SL, the copy of block kb+2 goes to slot (SL+2)%3.
+  auto step = [&](auto sl, int kb) {
+    constexpr int SL = decltype(sl)::value;
+    // a finished chunk of pooled values leaves first, so that its stores are
+    // older than this step's copy and never held up by the wait below
+    if (kb > 0 && kb % POOL_CHB == 0) flush(kb / POOL_CHB - 1);
+    dma(kb + 2, slot_ptr(std::integral_constant<int, (SL + 2) % 3>{}));  // slot of block kb-1: finished
 
-    f32x4 acc[8][4];
+    const bf16raw* kc = slot_ptr(sl);
+    const bool need_mask = kb * BLK + BLK - 1 > qt0 + 32 * wave;  // keys past some query of this wave
+    const int lim = tq - kb * BLK;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {  // 32-key tiles (other waves of the SIMD cover the MFMA chain)
+      f32x16 acc = zero16();
+      const int r = 32 * mt + l32;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero4();
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(&kc[r * DP + 8 * kswz<DP>(r, 2 * ks + h)]), bq[ks], acc);
+      // lane holds query column l32 and keys 32mt + 8(e/4) + 4h + e%4
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 a = ld8(&kbuf[cur][(16 * mt + l16) * LDK + 32 * ks + 8 * q4]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16(a, bq[nt][ks], acc[mt][nt]);
+      for (int e = 0; e < 16; ++e) {
+        float sv = acc[e];
+        if (need_mask && 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3) > lim) sv = -INFINITY;
+        mx = fmaxf(mx, sv);
       }
-
-    // Keys after a query exist only in blocks that reach past this wave's first query.
-    const bool need_mask = kb * BLK + BLK - 1 > qt0 + 64 * wave;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float m = -INFINITY;
-      const int lim = tq[nt] - kb * BLK;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = acc[mt][nt][e];
-          if (need_mask && 16 * mt + 4 * q4 + e > lim) s = -INFINITY;
-          m = fmaxf(m, s);
-        }
-      m = wave_max_xor_16_32(m);
+      __builtin_amdgcn_sched_barrier(0);  // keep later tiles' operand reads from piling up in registers
+    }
+    {
+      float m = fmaxf(mx, __shfl_xor(mx, 32));
       if (m == 0.0f) m = 0.0f;  // -0 and +0 rank equal
-      if (q4 == 0) pbuf[(64 * wave + 16 * nt + l16) * (POOL_CHB + 1) + (kb % POOL_CHB)] = m;
+      if (h == 0) pbuf[(kb / POOL_CHB) & 1][(32 * wave + l32) * PST + (kb % POOL_CHB)] = m;
     }
-    if (kb < kb_last) lstore(cur ^ 1);
-    __syncthreads();
-    if ((kb % POOL_CHB) == POOL_CHB - 1 || kb == kb_last) {
-      const int kb0 = kb - (kb % POOL_CHB);
-      for (int i = threadIdx.x; i < POOL_QT * POOL_CHB; i += 256) {
-        const int r = i / POOL_CHB, c = i % POOL_CHB, t = qt0 + r;
-        if (kb0 + c <= kb && t <= qlast && kb0 + c <= t / BLK)
-          pooled[((size_t)bg * W + (t - t0)) * N + kb0 + c] = pbuf[r * (POOL_CHB + 1) + c];
-      }
-      __syncthreads();
-    }
+    // block kb+1 must have landed: only this step's copy (NDMA per wave) may still be in flight
+    __builtin_amdgcn_s_waitcnt(0x0f70 | NDMA);
+    lds_barrier();
+  };
+
+  dma(0, kslot0);
+  dma(1, kslot1);
+  __builtin_amdgcn_s_waitcnt(0x0f70 | NDMA);  // vmcnt(NDMA): block 0 has landed (block 1 may be in flight)
+  lds_barrier();
+  // Three steps per pass without branches between them (a step past the last
+  // block recomputes the last block; the flush drops its values).
+  int kb = 0;
+  for (; kb <= kb_last; kb += 3) {
+    step(std::integral_constant<int, 0>{}, kb);
+    step(std::integral_constant<int, 1>{}, kb + 1);
+    step(std::integral_constant<int, 2>{}, kb + 2);
   }
+  if ((kb - 1) / POOL_CHB == kb_last / POOL_CHB) flush(kb_last / POOL_CHB);  // unless a step already did
+  // drain the ring copies still in flight before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 // Top-k of one pooled row per wavefront.  Scores become order-preserving u32
@@ -266,7 +298,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
 
 hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,
                              float* pooled, hipStream_t st) {
-  dim3 grid((w.W + POOL_QT - 1) / POOL_QT, g.B * g.G), block(256);
+  dim3 grid((w.W + POOL_QT - 1) / POOL_QT, g.B * g.G), block(64 * POOL_WAVES);
   switch (g.DP) {
     case 32: k_proxy_pool<32><<<grid, block, 0, st>>>(qp, kp, pooled, g.T, g.G, g.N, w.t0, w.W); break;
     case 64: k_proxy_pool<64><<<grid, block, 0, st>>>(qp, kp, pooled, g.T, g.G, g.N, w.t0, w.W); break;
