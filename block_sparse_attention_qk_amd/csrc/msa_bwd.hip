@@ -4,17 +4,19 @@
 // keyed on the cached block indices, xcelit "How MSA works").
 //
 // KV-stationary schedule, one work item per (batch, group, block) and window.
-// Eight waves (two per SIMD) share one 128-key block; wave (kq, hf) owns keys
-// [32kq, 32kq+32) and half hf of the tile rows and of the head dim.  Tiles of
-// 64 query rows (64/R tokens x R heads) stream through double-buffered LDS in
-// plain row-major form; the global loads of tile i+2 are in flight while tile
-// i computes.  Per tile (v_mfma_f32_32x32x16_bf16 throughout):
-//   S = Q K^T, dP = dO V^T        own 32 rows x own 32 keys
-//   P = exp(scale S - LSE), dS = scale P (dP - D)
-//   P^T, dS^T -> LDS              (so the other half's rows are visible)
-//   dV += P^T dO, dK += dS^T Q    own keys x own half of the head dim, all
-//                                 64 rows (dO, Q by LDS transpose reads)
-//   dQ^T = K^T dS^T               one 32 x 32 (head dim x rows) tile per wave
+// Eight waves share one 128-key block in two roles, one wave of each role per
+// SIMD, so that every SIMD always has a VALU-heavy and an MFMA-heavy wave:
+//   producers (waves 0-3), key quarter kq: for query tile i+1,
+//     S = Q K^T and dP = dO V^T (32 rows x its 32 keys; K, V rows in registers),
+//     P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D),
+//     P^T and dS^T -> LDS; and they gather the query rows of tile i+3.
+//   consumers (waves 4-7), key quarter kq: for tile i,
+//     dV += P^T dO, dK += dS^T Q   (its 32 keys x the whole head dim),
+//     dQ^T = K^T dS^T               (head-dim tile kq x the 32 rows),
+//   one barrier per tile.  Query tiles (32 rows = 32/R tokens x R heads) are
+// triple-buffered in LDS, P^T/dS^T double-buffered; every LDS tile is
+// XOR-swizzled on 16-byte chunks (v_mfma_f32_32x32x16_bf16 operands by 16-byte
+// reads and by ds_read_b64_tr_b16 transpose reads).
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
 // token's partials.  dK/dV are added into fp32 accumulators once per item.
 // Nothing is accumulated with atomics.
@@ -22,6 +24,7 @@
 #include "msa_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace msa {
 
@@ -33,10 +36,17 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (DCH - 1));
 }
 
+// Position of 16-byte chunk c of key row r in a P^T / dS^T tile (32 query rows
+// = 4 chunks per key row, four key rows per 256-byte bank line): the 8-byte
+// writes after the softmax, the 16-byte operand reads of dV/dK and the
+// transpose reads of dQ each spread evenly over the banks.
+__device__ __forceinline__ int pswz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
 constexpr int BWD_THREADS = 512;
+constexpr int BWD_TR = 32;  // query rows per tile
 
 template <int D, int R>
-__global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
+__global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     const bf16raw* __restrict__ q, const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
     const bf16raw* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int4* __restrict__ items, const int32_t* __restrict__ item_count, const int32_t* __restrict__ list,
@@ -44,21 +54,19 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
     int K, int t0, int W, int max_items, float scale, float sl2) {
   constexpr int KSD = D / 16;    // 32x32x16 k-steps over the head dim
   constexpr int NCT = D / 32;    // 32-wide head-dim tiles
-  constexpr int HCT = NCT / 2;   // head-dim tiles of dK/dV per wave
   constexpr int DCH = D / 8;     // 16-byte chunks per row
-  constexpr int TR = 64;         // query rows per tile
+  constexpr int TR = BWD_TR;     // query rows per tile
   constexpr int TT = TR / R;     // tokens per tile
-  constexpr int CPT = DCH / 8;   // chunks per thread per staged matrix (8 threads per row)
-  constexpr int LDP = TR + 8;    // P^T / dS^T row stride (bf16)
-  __shared__ __attribute__((aligned(16))) bf16raw Qs[2][TR * D];
-  __shared__ __attribute__((aligned(16))) bf16raw dOs[2][TR * D];
+  constexpr int CPT = DCH / 8;   // staged chunks per producer thread and matrix (8 threads per row)
   __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
-  __shared__ __attribute__((aligned(16))) bf16raw PT[BLK * LDP];
-  __shared__ __attribute__((aligned(16))) bf16raw dST[BLK * LDP];
-  __shared__ __attribute__((aligned(16))) float rlse[2][TR];
-  __shared__ __attribute__((aligned(16))) float rdd[2][TR];
-  __shared__ __attribute__((aligned(16))) int rlim[2][TR];
-  __shared__ __attribute__((aligned(16))) int rpair[2][TR];
+  __shared__ __attribute__((aligned(16))) bf16raw Qs[3][TR * D];
+  __shared__ __attribute__((aligned(16))) bf16raw dOs[3][TR * D];
+  __shared__ __attribute__((aligned(16))) bf16raw PT[2][BLK * TR];
+  __shared__ __attribute__((aligned(16))) bf16raw dST[2][BLK * TR];
+  __shared__ __attribute__((aligned(16))) float rlse[3][TR];
+  __shared__ __attribute__((aligned(16))) float rdd[3][TR];
+  __shared__ __attribute__((aligned(16))) int rlim[3][TR];
+  __shared__ __attribute__((aligned(16))) int rpair[3][TR];
 
   // Groups interleave in dispatch order (bg fastest) so that each group's
   // long early-block items start near the beginning of the launch.
@@ -68,21 +76,22 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
   const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
-  const int kq = wave & 3, hf = wave >> 2;
+  const int kq = wave & 3;
   const size_t kv0 = (size_t)(b * T + blk * BLK) * G + g;
   const size_t pair0 = (size_t)bg * W * K;
   const int32_t* lst = list + pair0 + start;
-  const int kown = 32 * kq + l32;  // this lane's key (B column of S, M row of dK/dV)
+  const int kown = 32 * kq + l32;  // this lane's key
   const int ntiles = (len + TT - 1) / TT;
 
-  // ---- K block -> LDS (swizzled row-major); own-key V rows -> registers
+  // ---- K block -> LDS (swizzled row-major), all threads: loads first, then stores
   {
-    constexpr int NLD = BLK * DCH / BWD_THREADS;  // 16-byte chunks per thread
+    constexpr int NLD = BLK * DCH / BWD_THREADS;
     uint4 kr[NLD];
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {  // all loads first, then all LDS stores
+    for (int u = 0; u < NLD; ++u) {
       const int c = tid + BWD_THREADS * u;
       kr[u] = ld16u(k + (kv0 + (size_t)(c / DCH) * G) * D + 8 * (c % DCH));
     }
@@ -92,181 +101,214 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_kv(
       st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], kr[u]);
     }
   }
-  bf16x8 bv[KSD];
-  {
-    const bf16raw* vr = v + (kv0 + (size_t)kown * G) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) bv[ks] = ld8(vr + 16 * ks);
-  }
-  f32x16 dka[HCT], dva[HCT];
-#pragma unroll
-  for (int c = 0; c < HCT; ++c) dka[c] = dva[c] = zero16();
 
-  // ---- staging of one tile: thread tid owns row tid/8 and chunks (tid%8) + 8u.
-  // Loads never branch and never wait where they are issued: a row past the
-  // list reads the list's last entry (finite data, masked at store time), the
-  // list entry of tile i+2 is fetched at the top of iteration i (no loaded
-  // value is carried across iterations), and scaling and validity are applied
-  // when the staged registers go to LDS, a full tile later.
-  const int srow = tid >> 3, ssub = tid & 7;
-  uint4 sq[CPT], sdo[CPT];
-  int s_li = len, s_pair = 0;
-  float s_lse = 0.f, s_dd = 0.f;
-  auto list_entry = [&](int ti) { return lst[min(ti * TT + srow / R, len - 1)]; };
-  auto stage_load = [&](int ti, int pair) {
-    s_li = ti * TT + srow / R;
-    s_pair = pair;
-    const int t = t0 + pair / K;
-    const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      sq[u] = ld16u(q + hrow * D + 8 * (ssub + 8 * u));
-      sdo[u] = ld16u(dout + hrow * D + 8 * (ssub + 8 * u));
-    }
-    s_lse = lse[hrow];
-    s_dd = Dd[hrow];
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int off = srow * D + 8 * swz<DCH>(srow, ssub + 8 * u);
-      st16u(&Qs[buf][off], sq[u]);
-      st16u(&dOs[buf][off], sdo[u]);
-    }
-    if (ssub == 0) {
-      const bool val = s_li < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
-      rlse[buf][srow] = val ? s_lse * LOG2E : INFINITY;
-      rdd[buf][srow] = s_dd * scale;
-      rlim[buf][srow] = val ? t0 + s_pair / K - blk * BLK : -1;
-      rpair[buf][srow] = val ? s_pair : -1;
-    }
-  };
-
-  if (ntiles > 0) {
-    stage_load(0, list_entry(0));
-    stage_store(0);
-  }
-  // All prologue loads (the V operand included) complete here, so that the
-  // loop's V operand uses carry no wait on later loads.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-#pragma unroll
-  for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bv[ks]));  // operand now defined by a non-memory op
-  if (ntiles > 0) stage_load(1, list_entry(1));
-  __syncthreads();
-
-  // dQ unit of this wave: head-dim tile qc, row tile qr (d = 64 has 4 units for 8 waves)
-  constexpr int QUNITS = NCT * 2;
-  const int qc = wave % NCT, qr = (wave / NCT) & 1;
-  const bool do_dq = wave < QUNITS;
-
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int cur = ti & 1;
-    const bf16raw* Qc = Qs[cur];
-    const bf16raw* dOc = dOs[cur];
-    const int pair2 = list_entry(ti + 2);  // consumed after barrier Y
-
-    // ---- S = Q K^T, dP = dO V^T : rows 32hf.., the wave's 32 keys
-    f32x16 sacc = zero16(), pacc = zero16();
+  if (wave < 4) {
+    // =================== producer ===================
+    // own-key K and V rows as B operands of S and dP (key kown, head dims 16ks + 8h .. +7)
+    bf16x8 bk[KSD], bv[KSD];
     {
-      const int r = 32 * hf + l32;
+      const bf16raw* kr = k + (kv0 + (size_t)kown * G) * D + 8 * h;
+      const bf16raw* vr = v + (kv0 + (size_t)kown * G) * D + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
-        const bf16x8 bk = ld8(&Ks[kown * D + 8 * swz<DCH>(kown, 2 * ks + h)]);
-        const int off = r * D + 8 * swz<DCH>(r, 2 * ks + h);
-        sacc = mfma32(ld8(&Qc[off]), bk, sacc);
-        pacc = mfma32(ld8(&dOc[off]), bv[ks], pacc);
+        bk[ks] = ld8(kr + 16 * ks);
+        bv[ks] = ld8(vr + 16 * ks);
       }
     }
-    // ---- P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D); lane
-    // holds key kown and rows 32hf + 8j + 4h + i
-    uint2 pw[4], dw[4];
+    // Staging: producer thread tid owns tile row tid/8 and chunks (tid%8) + 8u.
+    // Loads never branch and never wait where they are issued: a row past the
+    // list reads the list's last entry (finite data, masked at store time),
+    // the list entry of tile i+3 is fetched at the top of iteration i, and
+    // scaling and validity are applied when the staged registers go to LDS.
+    const int srow = tid >> 3, ssub = tid & 7;
+    uint4 sq[CPT], sdo[CPT];
+    int s_li = len, s_pair = 0;
+    float s_lse = 0.f, s_dd = 0.f;
+    auto list_entry = [&](int ti) { return lst[min(ti * TT + srow / R, len - 1)]; };
+    auto stage_load = [&](int ti, int pair) {
+      s_li = ti * TT + srow / R;
+      s_pair = pair;
+      const int t = t0 + pair / K;
+      const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r0 = 32 * hf + 8 * j + 4 * h;
-      const float4 lv = *reinterpret_cast<const float4*>(&rlse[cur][r0]);
-      const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[cur][r0]);
-      const int4 lm = *reinterpret_cast<const int4*>(&rlim[cur][r0]);
-      const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-      const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
-      float pv[4], dsv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * j + i;
-        const float ex = fast_exp2(sacc[e] * sl2 - la[i]);
-        pv[i] = kown <= ma[i] ? ex : 0.f;
-        dsv[i] = pv[i] * fmaf(pacc[e], scale, -da[i]);
+      for (int u = 0; u < CPT; ++u) {
+        sq[u] = ld16u(q + hrow * D + 8 * (ssub + 8 * u));
+        sdo[u] = ld16u(dout + hrow * D + 8 * (ssub + 8 * u));
       }
-      pw[j] = make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]));
-      dw[j] = make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3]));
+      s_lse = lse[hrow];
+      s_dd = Dd[hrow];
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int off = srow * D + 8 * swz<DCH>(srow, ssub + 8 * u);
+        st16u(&Qs[buf][off], sq[u]);
+        st16u(&dOs[buf][off], sdo[u]);
+      }
+      if (ssub == 0) {
+        const bool val = s_li < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
+        rlse[buf][srow] = val ? s_lse * LOG2E : INFINITY;
+        rdd[buf][srow] = s_dd * scale;
+        rlim[buf][srow] = val ? t0 + s_pair / K - blk * BLK : -1;
+        rpair[buf][srow] = val ? s_pair : -1;
+      }
+    };
+
+    stage_load(0, list_entry(0));
+    stage_store(0);
+    // All prologue loads (K and V operands included) complete here, so that the
+    // loop's waits count only its own traffic.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bk[ks]), "+v"(bv[ks]));
+    stage_load(1, list_entry(1));
+    __syncthreads();
+
+    // One iteration: compute tile i+1, stage tile i+2, load tile i+3.  The
+    // buffer indices are compile-time constants in each copy of the 6-way
+    // unrolled loop ((i+1) mod 3, (i+1) mod 2 and (i+2) mod 3).
+    auto produce = [&](auto qbc, auto pbc, auto sbc, int i) {
+      constexpr int qb = decltype(qbc)::value, pb = decltype(pbc)::value, sb = decltype(sbc)::value;
+      const int pair3 = list_entry(i + 3);  // consumed by this iteration's staging load
+      if (i + 1 < ntiles) {
+        const bf16raw* Qc = Qs[qb];
+        const bf16raw* dOc = dOs[qb];
+        f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+          const int off = l32 * D + 8 * swz<DCH>(l32, 2 * ks + h);
+          sacc = mfma32(ld8(&Qc[off]), bk[ks], sacc);
+          pacc = mfma32(ld8(&dOc[off]), bv[ks], pacc);
+        }
+        // lane holds key kown and rows 8jj + 4h + ii
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r0 = 8 * jj + 4 * h;
+          const float4 lv = *reinterpret_cast<const float4*>(&rlse[qb][r0]);
+          const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[qb][r0]);
+          const int4 lm = *reinterpret_cast<const int4*>(&rlim[qb][r0]);
+          const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+          const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int e = 4 * jj + ii;
+            const float ex = fast_exp2(sacc[e] * sl2 - la[ii]);
+            pv[ii] = kown <= ma[ii] ? ex : 0.f;
+            dsv[ii] = pv[ii] * fmaf(pacc[e], scale, -da[ii]);
+          }
+          const int o = kown * TR + 8 * pswz(kown, jj) + 4 * h;
+          *reinterpret_cast<uint2*>(&PT[pb][o]) = make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]));
+          *reinterpret_cast<uint2*>(&dST[pb][o]) = make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3]));
+        }
+      }
+      stage_store(sb);  // tile i+2 (rows past the list are masked)
+      stage_load(i + 3, pair3);
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int i0 = -1; i0 < ntiles; i0 += 6) {  // i0 = -1 (mod 6): i0 + u computes tile 6m + u
+      produce(I0{}, I0{}, I1{}, i0);
+      if (i0 + 1 < ntiles) produce(I1{}, I1{}, I2{}, i0 + 1);
+      if (i0 + 2 < ntiles) produce(I2{}, I0{}, I0{}, i0 + 2);
+      if (i0 + 3 < ntiles) produce(I0{}, I1{}, I1{}, i0 + 3);
+      if (i0 + 4 < ntiles) produce(I1{}, I0{}, I2{}, i0 + 4);
+      if (i0 + 5 < ntiles) produce(I2{}, I1{}, I0{}, i0 + 5);
+    }
+  } else {
+    // =================== consumer ===================
+    f32x16 dka[NCT], dva[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) dka[c] = dva[c] = zero16();
+    __syncthreads();  // K block and tile 0 staged
+
+    // One tile: the buffer indices are compile-time constants in each copy of
+    // the 6-way unrolled loop (i mod 3 and i mod 2), so every LDS address is a
+    // lane offset plus an immediate.
+    auto consume = [&](auto qbc, auto pbc, int i) {
+      constexpr int qb = decltype(qbc)::value, pb = decltype(pbc)::value;
+      if (i >= 0) {
+        const bf16raw* Qc = Qs[qb];
+        const bf16raw* dOc = dOs[qb];
+        // ---- dV += P^T dO, dK += dS^T Q : own keys x all head-dim tiles, the tile's 32 rows
+#pragma unroll
+        for (int st = 0; st < TR / 16; ++st) {
+          const bf16x8 ap = ld8(&PT[pb][kown * TR + 8 * pswz(kown, 2 * st + h)]);
+          const bf16x8 ad = ld8(&dST[pb][kown * TR + 8 * pswz(kown, 2 * st + h)]);
+          const int ra = 16 * st + 8 * h + (i16 >> 2);  // rows of the first transpose read
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) {
+            const int col = 32 * c + 16 * g16 + 4 * (i16 & 3);
+            const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
+            const int ob = (ra + 4) * D + 8 * swz<DCH>(ra + 4, col >> 3) + (col & 7);
+            const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
+            const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
+            dva[c] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[c]);
+            dka[c] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[c]);
+          }
+        }
+        // ---- dQ^T tile = K^T dS^T : head-dim tile kq along M, the 32 rows along N, keys as K
+        if (kq < NCT) {
+          f32x16 dq = zero16();
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const int kr = 16 * ks + 8 * h + (i16 >> 2);
+            const int col = 32 * kq + 16 * g16 + 4 * (i16 & 3);
+            const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
+            const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
+            const int rc = 16 * g16 + 4 * (i16 & 3);
+            const uint2 b0 = lds_tr4(&dST[pb][kr * TR + 8 * pswz(kr, rc >> 3) + (rc & 7)]);
+            const uint2 b1 = lds_tr4(&dST[pb][(kr + 4) * TR + 8 * pswz(kr + 4, rc >> 3) + (rc & 7)]);
+            dq = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq);
+          }
+          // lane holds row l32, head-dim columns 32kq + 8j + 4h + (0..3)
+          const int p = rpair[qb][l32];
+          if (p >= 0) {
+            bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + l32 % R) * D + 32 * kq + 4 * h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st4bf(dst + 8 * j, dq[4 * j], dq[4 * j + 1], dq[4 * j + 2], dq[4 * j + 3]);
+          }
+        }
+      }
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int i0 = -1; i0 < ntiles; i0 += 6) {  // i0 = -1 (mod 6): i0 + u has i mod 3 = (u+2)%3, i mod 2 = (u+1)%2
+      consume(I2{}, I1{}, i0);
+      if (i0 + 1 < ntiles) consume(I0{}, I0{}, i0 + 1);
+      if (i0 + 2 < ntiles) consume(I1{}, I1{}, i0 + 2);
+      if (i0 + 3 < ntiles) consume(I2{}, I0{}, i0 + 3);
+      if (i0 + 4 < ntiles) consume(I0{}, I1{}, i0 + 4);
+      if (i0 + 5 < ntiles) consume(I1{}, I0{}, i0 + 5);
     }
 
-    __syncthreads();  // X: previous tile's P^T/dS^T, Q/dO[cur^1] and row data are no longer read
+    // ---- dK, dV of the owned keys: lane holds head-dim column 32c + l32, keys 32kq + 8j + 4h + i.
+    // Per head-dim tile, all 32 accumulator reads are issued before the stores.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = kown * LDP + 32 * hf + 8 * j + 4 * h;
-      *reinterpret_cast<uint2*>(&PT[o]) = pw[j];
-      *reinterpret_cast<uint2*>(&dST[o]) = dw[j];
-    }
-    stage_store(cur ^ 1);  // tile ti+1 (zeros past the list)
-    __syncthreads();       // Y: P^T, dS^T and the next tile are in LDS
-    stage_load(ti + 2, pair2);
-
-    // ---- dV += P^T dO, dK += dS^T Q : own keys x head-dim tiles hf*HCT.., all 64 rows
+    for (int c = 0; c < NCT; ++c) {
+      float ok[16], ov[16];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 ap = ld8(&PT[kown * LDP + 16 * st + 8 * h]);
-      const bf16x8 ad = ld8(&dST[kown * LDP + 16 * st + 8 * h]);
-      const int ra = 16 * st + 8 * h + (i16 >> 2);  // rows of the first transpose read
-#pragma unroll
-      for (int c = 0; c < HCT; ++c) {
-        const int col = 32 * (hf * HCT + c) + 16 * g16 + 4 * (i16 & 3);
-        const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
-        const int ob = (ra + 4) * D + 8 * swz<DCH>(ra + 4, col >> 3) + (col & 7);
-        const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
-        const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
-        dva[c] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[c]);
-        dka[c] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[c]);
+      for (int e = 0; e < 16; ++e) {
+        const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
+        const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
+        ok[e] = dk_acc[off];
+        ov[e] = dv_acc[off];
       }
-    }
-
-    // ---- dQ^T tile = K^T dS^T : head-dim tile qc along M, row tile qr along N, keys as K
-    if (do_dq) {
-      f32x16 dq = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int kr = 16 * ks + 8 * h + (i16 >> 2);
-        const int col = 32 * qc + 16 * g16 + 4 * (i16 & 3);
-        const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
-        const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
-        const int rc = 32 * qr + 16 * g16 + 4 * (i16 & 3);
-        const uint2 b0 = lds_tr4(&dST[kr * LDP + rc]);
-        const uint2 b1 = lds_tr4(&dST[(kr + 4) * LDP + rc]);
-        dq = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq);
-      }
-      // lane holds row 32qr + l32, head-dim columns 32qc + 8j + 4h + (0..3)
-      const int row = 32 * qr + l32;
-      const int p = rpair[cur][row];
-      if (p >= 0) {
-        bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + row % R) * D + 32 * qc + 4 * h;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st4bf(dst + 8 * j, dq[4 * j], dq[4 * j + 1], dq[4 * j + 2], dq[4 * j + 3]);
+      for (int e = 0; e < 16; ++e) {
+        const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
+        const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
+        dk_acc[off] = ok[e] + dka[c][e];
+        dv_acc[off] = ov[e] + dva[c][e];
       }
     }
   }
-
-  // ---- dK, dV of the owned keys: lane holds head-dim column 32ct + l32, keys 32kq + 8j + 4h + i
-#pragma unroll
-  for (int c = 0; c < HCT; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
-      const size_t off = (kv0 + (size_t)kk * G) * D + 32 * (hf * HCT + c) + l32;
-      dk_acc[off] += dka[c][e];
-      dv_acc[off] += dva[c][e];
-    }
 }
 
-// D[row] = dot(dout[row], o[row]) over the head dim, fp32; D/8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_dot(const bf16raw* __restrict__ o, const bf16raw* __restrict__ dout,
                                                  float* __restrict__ Dd, size_t rows) {
