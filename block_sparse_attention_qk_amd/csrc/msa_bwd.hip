@@ -263,12 +263,23 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
             const uint2 b1 = lds_tr4(&dST[pb][(kr + 4) * TR + 8 * pswz(kr + 4, rc >> 3) + (rc & 7)]);
             dq = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq);
           }
-          // lane holds row l32, head-dim columns 32kq + 8j + 4h + (0..3)
-          const int p = rpair[qb][l32];
-          if (p >= 0) {
-            bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + l32 % R) * D + 32 * kq + 4 * h;
+          // lane holds row l32, head-dim columns 32kq + 8j + 4h + (0..3); one lane
+          // swap per dword gives lane half h whole 16-byte runs (columns 16pp + 8h .. +7)
+          uint4 run[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st4bf(dst + 8 * j, dq[4 * j], dq[4 * j + 1], dq[4 * j + 2], dq[4 * j + 3]);
+          for (int pp = 0; pp < 2; ++pp) {
+            const int e0 = 8 * pp, e1 = 8 * pp + 4;
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pack2(dq[e0], dq[e0 + 1]), pack2(dq[e1], dq[e1 + 1]),
+                                                             false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pack2(dq[e0 + 2], dq[e0 + 3]),
+                                                             pack2(dq[e1 + 2], dq[e1 + 3]), false, false);
+            run[pp] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
+          const int p = rpair[qb][l32];  // the same for both lane halves of a row
+          if (p >= 0) {
+            bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + l32 % R) * D + 32 * kq + 8 * h;
+            st16u(dst, run[0]);
+            st16u(dst + 16, run[1]);
           }
         }
       }

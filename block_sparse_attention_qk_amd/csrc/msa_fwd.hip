@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   constexpr int TT = 128 / R;   // tokens per 128-row tile
   __shared__ __attribute__((aligned(16))) bf16raw Ks[BLK * D];
   __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
+  __shared__ int lsts[FWD_ITEM_TOKENS];  // the item's pair list (items hold at most FWD_ITEM_TOKENS pairs)
 
   // Groups interleave in dispatch order (bg fastest) so that each group's
   // long early-block items start near the beginning of the launch.
@@ -73,16 +74,17 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
       st16u(&Ks[r * D + 8 * fswz<DCH>(r, cc)], kr[u]);
       st16u(&Vs[r * D + 8 * fswz<DCH>(r, cc)], vr[u]);
     }
+    for (int i = tid; i < len; i += 256) lsts[i] = lst[i];
   }
 
   // this lane's query row within a tile and its Q operand (B of S^T: column = row).
   // Loads never branch: a row past the list reads the list's last entry
-  // (finite data; its result is dropped).  The list entry of tile i+1 is
-  // fetched at the top of iteration i and used after the softmax, so the row
-  // address does not wait on memory and no loaded value crosses iterations.
+  // (finite data; its result is dropped).  The list entries come from LDS, so
+  // the only global loads in the loop are the Q rows: waiting for them never
+  // waits for the partial stores issued after them.
   const int row = 32 * wave + l32;
   const int tt = row / R, hh = row % R;
-  auto list_entry = [&](int ti) { return lst[min(ti * TT + tt, len - 1)]; };
+  auto list_entry = [&](int ti) { return lsts[min(ti * TT + tt, len - 1)]; };
   auto load_q = [&](int ti, int pair, bf16x8* bq, int& pr, int& lim) {
     const bool val = ti * TT + tt < len;
     const int t = t0 + pair / K;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   const int ntiles = (len + TT - 1) / TT;
   bf16x8 bq[KSD];
   int pr = -1, lim = BLK - 1;
-  if (ntiles > 0) load_q(0, list_entry(0), bq, pr, lim);
+  if (ntiles > 0) load_q(0, lst[min(tt, len - 1)], bq, pr, lim);
   // The prologue's loads complete here and the first Q operand is redefined
   // by a non-memory op, so that the loop's waits count only its own traffic.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   __syncthreads();
 
   for (int ti = 0; ti < ntiles; ++ti) {
-    const int pair1 = list_entry(ti + 1);  // consumed after the softmax
+    const int pair1 = list_entry(ti + 1);
     // S^T = K Q^T: 4 key tiles of 32 along M, this wave's 32 rows along N
     f32x16 acc[4];
 #pragma unroll
@@ -180,13 +182,23 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
     {
       const float inv = 1.0f / l;
       const size_t pidx = cpr >= 0 ? pair0 + (size_t)cpr : (size_t)BG * W * K;
-      bf16raw* dst = part_o + (pidx * R + hh) * D + 4 * h;
+      // Lane halves h = 0/1 hold head-dim columns 8j + 0..3 / 8j + 4..7 of the
+      // same row; one lane swap per dword gives lane h whole 16-byte runs
+      // (columns 16p + 8h .. +7 of each 32-column tile), stored as one 16-byte write.
+      bf16raw* dst = part_o + (pidx * R + hh) * D + 8 * h;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          st4bf(dst + 32 * ct + 8 * j, oacc[ct][4 * j] * inv, oacc[ct][4 * j + 1] * inv, oacc[ct][4 * j + 2] * inv,
-                oacc[ct][4 * j + 3] * inv);
+        for (int pp = 0; pp < 2; ++pp) {
+          const int e0 = 8 * pp, e1 = 8 * pp + 4;  // columns 16pp + 4h + 0..3 and 16pp + 8 + 4h + 0..3
+          const uint32_t u0 = pack2(oacc[ct][e0] * inv, oacc[ct][e0 + 1] * inv);
+          const uint32_t u1 = pack2(oacc[ct][e0 + 2] * inv, oacc[ct][e0 + 3] * inv);
+          const uint32_t w0 = pack2(oacc[ct][e1] * inv, oacc[ct][e1 + 1] * inv);
+          const uint32_t w1 = pack2(oacc[ct][e1 + 2] * inv, oacc[ct][e1 + 3] * inv);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(u0, w0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(u1, w1, false, false);
+          st16u(dst + 32 * ct + 16 * pp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+        }
       part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;  // both lane halves hold the same value
     }
   }
