@@ -15,7 +15,7 @@ per-phase and per-kernel times (HIP events recorded by the library on the
 launch stream), the roofline of the dominant kernel, the 1M configuration as
 a second workload, and the CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m|''] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern|''] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -150,15 +150,22 @@ def gpu_inputs(cfg: synth.Config, seed: int = 0) -> dict:
     return out
 
 
-def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool) -> dict:
+PATTERN = (8, 64)  # window blocks, dilation: the fixed-pattern leg (united with the proxy top-k)
+
+
+def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, pattern=None) -> dict:
+    """One step = proxy select (+ the fixed window/dilation pattern united with
+    it, when `pattern` is given) + forward + backward over the cache."""
     if host_inputs:
         x = {n: t.cuda() for n, t in synth.make_inputs(cfg).items()}
     else:
         x = gpu_inputs(cfg)
-    dims = (cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    width = msa.pattern_width(cfg.T, pattern[0], pattern[1], cfg.topk) if pattern else cfg.topk
+    dims = (cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, width)
     ws_bytes = max(msa.msa_workspace_bytes(*dims, op) for op in (msa.OP_SELECT, msa.OP_FWD, msa.OP_BWD))
     ws = msa.Workspace(nbytes=ws_bytes)
     idx = torch.empty((cfg.B, cfg.G, cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
+    idx_main = torch.empty((cfg.B, cfg.G, cfg.T, width), dtype=torch.int32, device="cuda") if pattern else idx
     o = torch.empty_like(x["q"])
     lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
@@ -166,17 +173,22 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool) 
         if ev:
             ev[0].record()
         msa.msa_proxy_select(x["qp"], x["kp"], cfg.topk, ws=ws, out=idx)
+        if pattern:
+            msa.msa_pattern_select(cfg.B, cfg.T, cfg.G, pattern[0], pattern[1], idx_in=idx, width=width,
+                                   out=idx_main)
         if ev:
             ev[1].record()
-        msa.msa_fwd(x["q"], x["k"], x["v"], idx, ws=ws, out=(o, lse))
+        msa.msa_fwd(x["q"], x["k"], x["v"], idx_main, ws=ws, out=(o, lse))
         if ev:
             ev[2].record()
-        msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, ws=ws, out=(dq, dk, dv))
+        msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx_main, ws=ws, out=(dq, dk, dv))
         if ev:
             ev[3].record()
 
     for _ in range(warmup):
         step()
+    # pairs actually read by the Main Branch (the pattern's rows vary in length)
+    pairs = int((idx_main >= 0).sum().item()) if pattern else cfg.pairs()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     msa.timing_enable(True)
@@ -197,11 +209,12 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool) 
     tokens = cfg.B * cfg.T
     ms_step = total_ms / steps
     t_sel, t_fwd, t_bwd = (p / steps for p in phase)
-    f_fwd, f_bwd, f_proxy = cfg.flops_fwd(), cfg.flops_bwd(), cfg.flops_proxy()
-    pairs = cfg.pairs()
+    f_pair = 4 * cfg.d * cfg.R * 128  # forward flop per (token, group, block); backward is 2.5x
+    f_fwd, f_bwd, f_proxy = f_pair * pairs, 2.5 * f_pair * pairs, cfg.flops_proxy()
     res = {
-        "workload": cfg.name,
-        "shape": {"B": cfg.B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk},
+        "workload": cfg.name + ("+pattern(window=%d,dilation=%d)" % pattern if pattern else ""),
+        "shape": {"B": cfg.B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk,
+                  "cache_width": width},
         "ms_per_step": ms_step,
         "wall_ms_per_step": 1e3 * wall / steps,
         "tokens_per_s": tokens / (ms_step / 1e3),
@@ -215,13 +228,13 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool) 
         "kernel_launches_per_step": {k: v[1] / steps for k, v in kern.items()},
     }
     res["fwd_bwd_frac_of_peak"] = res["fwd_bwd_effective_tflops"] / PEAK_BF16_TFLOPS
-    res["roofline"] = roofline(cfg, kern, steps)
+    res["roofline"] = roofline(cfg, kern, steps, pairs)
     del x, ws, idx, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
     return res
 
 
-def roofline(cfg: synth.Config, kern: dict, steps: int) -> dict:
+def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int) -> dict:
     """Roofline entry of the kernel with the largest time: algorithmic work per
     launch divided by its average launch duration."""
     name = max(kern, key=lambda k: kern[k][0])
@@ -229,15 +242,16 @@ def roofline(cfg: synth.Config, kern: dict, steps: int) -> dict:
     avg_s = ms / max(launches, 1) / 1e3
     per_step_launch = launches / steps
     BG = cfg.B * cfg.G
+    f_pair = 4 * cfg.d * cfg.R * 128
     if name == "bwd_partials":
-        work, bound, unit = cfg.flops_bwd() / per_step_launch, "mfma", "TFLOP/s"
+        work, bound, unit = 2.5 * f_pair * pairs / per_step_launch, "mfma", "TFLOP/s"
     elif name == "fwd_partials":
-        work, bound, unit = cfg.flops_fwd() / per_step_launch, "mfma", "TFLOP/s"
+        work, bound, unit = f_pair * pairs / per_step_launch, "mfma", "TFLOP/s"
     elif name == "proxy_pool":
         work, bound, unit = cfg.flops_proxy() / per_step_launch, "mfma", "TFLOP/s"
     elif name in ("fwd_combine", "dq_combine"):
         # read every partial (bf16) once, write the bf16 result (+ lse for fwd)
-        work = (cfg.pairs() * cfg.R * cfg.d * 2 + cfg.B * cfg.T * cfg.H * cfg.d * 2) / per_step_launch
+        work = (pairs * cfg.R * cfg.d * 2 + cfg.B * cfg.T * cfg.H * cfg.d * 2) / per_step_launch
         bound, unit = "hbm", "GB/s"
     else:
         work = float("nan")
@@ -292,7 +306,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--also", default="1m", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--also", default="1m,pattern",
+                    help="comma list of extra workloads: config names, or 'pattern' (the main config with the fixed "
+                         "window/dilation pattern united with the proxy top-k); '' for none")
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -327,6 +343,11 @@ def main() -> int:
     print("bench: main workload done: %.3f ms/step" % main_res["ms_per_step"], file=sys.stderr, flush=True)
     extra = []
     for name in [s for s in args.also.split(",") if s and s != args.config]:
+        if name == "pattern":
+            print("bench: extra workload %s + pattern %s" % (cfg, PATTERN), file=sys.stderr, flush=True)
+            extra.append(run_workload(cfg, args.steps, 2, host_inputs=False, pattern=PATTERN))
+            print("bench: pattern done: %.1f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
+            continue
         c = synth.CONFIGS[name]
         print("bench: extra workload %s" % (c,), file=sys.stderr, flush=True)
         extra.append(run_workload(c, args.also_steps, 1, host_inputs=False))

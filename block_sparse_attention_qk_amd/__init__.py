@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
-    "msa_proxy_select", "msa_fwd", "msa_bwd", "OP_SELECT", "OP_FWD", "OP_BWD", "EXPORTED_SYMBOLS",
+    "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "OP_SELECT", "OP_FWD", "OP_BWD", "EXPORTED_SYMBOLS",
     "KERNEL_NAMES", "timing_enable", "timing_read",
 ]
 
@@ -34,12 +34,13 @@ _LIB_PATH = os.path.join(_HERE, "libmsa.so")
 _lib = None
 
 OP_SELECT, OP_FWD, OP_BWD = 0, 1, 2
-EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_fwd",
-                    "msa_bwd", "msa_status_str", "msa_version", "msa_timing_enable", "msa_timing_read")
+EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_pattern_select",
+                    "msa_fwd", "msa_bwd", "msa_status_str", "msa_version", "msa_timing_enable",
+                    "msa_timing_read")
 
 # msa_kernel_id values (include/msa.h)
 KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
-                "dq_combine", "convert")
+                "dq_combine", "convert", "pattern")
 
 
 class MsaError(RuntimeError):
@@ -70,9 +71,10 @@ def load():
     lib.msa_workspace_min_bytes.argtypes = [D, I]
     lib.msa_workspace_min_bytes.restype = SZ
     lib.msa_proxy_select.argtypes = [D, P, P, P, P, SZ, P]
+    lib.msa_pattern_select.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
     lib.msa_fwd.argtypes = [D, P, P, P, P, P, P, P, SZ, P]
     lib.msa_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
-    for f in ("msa_proxy_select", "msa_fwd", "msa_bwd"):
+    for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd"):
         getattr(lib, f).restype = I
     lib.msa_status_str.argtypes = [I]
     lib.msa_status_str.restype = ctypes.c_char_p
@@ -177,6 +179,36 @@ def msa_proxy_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, ws: Optional
     _check(lib.msa_proxy_select(ctypes.byref(dims), _ptr(qp), _ptr(kp), _ptr(idx), _ptr(w), w.numel(),
                                 _stream(qp.device)))
     return idx
+
+
+def pattern_width(T: int, window: int, dilation: int, k_in: int = 0) -> int:
+    """Largest row msa_pattern_select can produce (the smallest accepted output width)."""
+    N = T // 128
+    far = (max(0, N - window) + dilation - 1) // dilation if dilation > 0 else 0
+    return min(N, min(window, N) + far + k_in)
+
+
+def msa_pattern_select(B: int, T: int, G: int, window: int, dilation: int, idx_in: Optional[torch.Tensor] = None,
+                       width: Optional[int] = None, device=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fixed window/dilation block pattern, optionally united with the cache idx_in [B,G,T,k_in]:
+    returns the block-index cache [B,G,T,width] int32 (ascending, -1 padded)."""
+    k_in = 0
+    if idx_in is not None:
+        _need(idx_in, "idx_in", torch.int32, 4)
+        if tuple(idx_in.shape[:3]) != (B, G, T):
+            raise ValueError("idx_in shape %s does not match [B,G,T,*] = [%d,%d,%d,*]" % (tuple(idx_in.shape), B, G, T))
+        k_in = idx_in.shape[3]
+        device = idx_in.device
+    if width is None:
+        width = pattern_width(T, window, dilation, k_in)
+    if out is None:
+        out = torch.empty((B, G, T, width), dtype=torch.int32, device=device if device is not None else "cuda")
+    _need(out, "out", torch.int32, 4)
+    dims = _dims(B, T, G, G, 64, 32, width, 0.0)
+    _check(load().msa_pattern_select(ctypes.byref(dims), int(window), int(dilation),
+                                     _ptr(idx_in) if idx_in is not None else None, int(k_in), _ptr(out),
+                                     _stream(out.device)))
+    return out
 
 
 def _main_dims(q, k, idx, scale) -> Tuple[_Dims, int, int, int, int, int, int]:

@@ -1,6 +1,7 @@
 // C ABI of libmsa (declared in include/msa.h): host-side argument checks,
 // workspace layout, the walk over token windows, and the kernel chain of each
 // entry point on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -187,6 +188,30 @@ size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op) {
   Geo g;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
   return layout(g, op, min_window(g)).total;
+}
+
+msa_status msa_pattern_select(const msa_dims* dims, int32_t window, int32_t dilation, const int32_t* idx_in,
+                              int32_t k_in, int32_t* idx_out, void* stream) {
+  if (!dims) return MSA_ERR_NULL;
+  const msa_dims& d = *dims;
+  if (d.B < 1 || d.T < 128 || d.T % 128 != 0 || d.T > (1 << 20) || d.G < 1 || d.topk < 1 || d.topk > 1024)
+    return MSA_ERR_SHAPE;
+  if ((int64_t)d.T * d.topk >= ((int64_t)1 << 31) || (int64_t)d.B * d.T >= ((int64_t)1 << 30))
+    return MSA_ERR_SHAPE;
+  if (window < 0 || dilation < 0) return MSA_ERR_SHAPE;
+  if (window == 0 && dilation == 0 && idx_in == nullptr) return MSA_ERR_SHAPE;
+  if (idx_in != nullptr && (k_in < 1 || k_in > 1024)) return MSA_ERR_SHAPE;
+  if (!idx_out) return MSA_ERR_NULL;
+  if (!al16(idx_out) || (idx_in && !al16(idx_in))) return MSA_ERR_ALIGN;
+  // the largest row the pattern can produce must fit the output width
+  const int64_t N = d.T / 128, w = std::min<int64_t>(window, N);
+  const int64_t far = dilation > 0 ? (std::max<int64_t>(0, N - window) + dilation - 1) / dilation : 0;
+  const int64_t bound = std::min<int64_t>(N, w + far + (idx_in ? k_in : 0));
+  if (d.topk < bound) return MSA_ERR_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  MSA_LAUNCH(MSA_K_PATTERN, st,
+             launch_pattern(idx_in, idx_in ? k_in : 0, idx_out, d.topk, d.B, d.G, d.T, window, dilation, st));
+  return MSA_OK;
 }
 
 msa_status msa_proxy_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp, int32_t* idx, void* ws,

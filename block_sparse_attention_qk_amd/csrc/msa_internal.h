@@ -55,5 +55,7 @@ hipError_t launch_bwd_partials(const Geo& g, const Win& w, const uint16_t* q, co
 hipError_t launch_dq_combine(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* dq_part,
                              uint16_t* dq, hipStream_t st);
 hipError_t launch_cvt_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
+hipError_t launch_pattern(const int32_t* idx_in, int k_in, int32_t* idx_out, int K, int B, int G, int T,
+                          int window, int dilation, hipStream_t st);
 
 }  // namespace msa

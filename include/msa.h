@@ -99,6 +99,28 @@ size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op);
 msa_status msa_proxy_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp,
                             int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+/* Fixed block pattern (keelcrux "Flash-MSA: Train on a million tokens without
+ * breaking the compute bank", section "Under the hood": the block pattern is
+ * configurable by window size and dilation; the pages define neither, this is
+ * the reading).  For every (b, g, t), with nc = t/128 + 1 causal blocks, the
+ * row idx_out[b,g,t,:] lists once each, in ascending order:
+ *   - the `window` most recent causal blocks, max(0, nc - window) .. nc - 1;
+ *   - each causal block below the window whose index is a multiple of
+ *     `dilation` (none when dilation == 0);
+ *   - when idx_in != NULL, each entry of idx_in[b,g,t,0..k_in) that is a
+ *     causal block (other entries, -1 included, are ignored), so a proxy top-k
+ *     cache can be united with the pattern;
+ * and the row is padded with -1 to width dims->topk.  Only B, T, G and topk of
+ * dims are read.  Requirements (MSA_ERR_SHAPE otherwise): window >= 0,
+ * dilation >= 0, at least one of window, dilation, idx_in selects blocks
+ * (window > 0 or dilation > 0 or idx_in != NULL, so that msa_fwd gets a valid
+ * cache when idx_in rows are valid), 1 <= k_in <= 1024 when idx_in is given,
+ * and dims->topk >= min(N, min(window, N) + ceil(max(0, N - window) / dilation)
+ * + k_in) with N = T/128 (the largest row the pattern can produce).  No
+ * workspace; idx_in and idx_out must not overlap. */
+msa_status msa_pattern_select(const msa_dims* dims, int32_t window, int32_t dilation, const int32_t* idx_in,
+                              int32_t k_in, int32_t* idx_out, void* stream);
+
 /* Main Branch forward.  For every (b, t, h), g = h / (H/G), over the key set
  * J = { j <= t : j/128 is listed in idx[b,g,t,:] } and s_j = scale * q.k_j:
  *   o[b,t,h,:] = sum_j softmax(s)_j v[b,j,g,:]   (bf16, round to nearest even)
@@ -141,7 +163,8 @@ typedef enum {
   MSA_K_BWD_PARTIALS = 6, /* backward dK/dV + per-pair dQ partials (KV-stationary) */
   MSA_K_DQ_COMBINE = 7,   /* dQ partial sums */
   MSA_K_CONVERT = 8,      /* fp32 -> bf16 of dK, dV */
-  MSA_K_COUNT = 9
+  MSA_K_PATTERN = 9,      /* fixed window/dilation pattern (msa_pattern_select) */
+  MSA_K_COUNT = 10
 } msa_kernel_id;
 
 /* on != 0 enables timing; any call clears what was recorded. */

@@ -207,3 +207,34 @@ def bwd(dm: Dims, q, k, v, dout, idx):
     _check(lib.msa_oracle_bwd(ctypes.byref(cd), _ptr(q64), _ptr(k64), _ptr(v64), _ptr(do64),
                               _ptr(ix), _ptr(dq), _ptr(dk), _ptr(dv)), "bwd")
     return dq, dk, dv
+
+
+def pattern_select(B: int, T: int, G: int, window: int, dilation: int, width: int, idx_in=None) -> np.ndarray:
+    """Fixed window/dilation block pattern, optionally united with a cache.
+
+    Follows the reading of keelcrux "Flash-MSA: Train on a million tokens without
+    breaking the compute bank", section "Under the hood" (the block pattern is
+    configurable by window size and dilation; the page defines neither): for
+    query t with nc = t//128 + 1 causal blocks, the row holds, once each and in
+    ascending order, the `window` most recent causal blocks, every causal block
+    below the window whose index is a multiple of `dilation` (none when 0), and
+    the causal entries of idx_in[b, g, t, :]; the rest of the row is -1.
+    Plain per-row set construction (test infrastructure only).
+    """
+    out = np.full((B, G, T, width), -1, dtype=np.int32)
+    ii = None if idx_in is None else _i32(idx_in)
+    for b in range(B):
+        for g in range(G):
+            for t in range(T):
+                nc = t // BLOCK + 1
+                lo = max(0, nc - window)
+                chosen = set(range(lo, nc))
+                if dilation > 0:
+                    chosen.update(blk for blk in range(0, lo) if blk % dilation == 0)
+                if ii is not None:
+                    chosen.update(int(blk) for blk in ii[b, g, t] if 0 <= blk < nc)
+                row = sorted(chosen)
+                if len(row) > width:
+                    raise ValueError("pattern row of %d blocks exceeds width %d" % (len(row), width))
+                out[b, g, t, :len(row)] = row
+    return out

@@ -165,3 +165,24 @@ def test_binding_rejects_host_tensors(msa):
     idx = torch.zeros((1, 2, 256, 2), dtype=torch.int32)
     with pytest.raises(ValueError):
         msa.msa_fwd(q, x, x, idx)
+
+
+def test_pattern_select_checks(lib, msa):
+    P = ctypes.c_void_p(4096)
+    d = _dims(msa, T=1024, topk=8)
+    sel = lib.msa_pattern_select
+    assert sel(None, 2, 3, None, 0, P, None) == ERR_NULL
+    assert sel(ctypes.byref(d), 2, 3, None, 0, None, None) == ERR_NULL
+    assert sel(ctypes.byref(d), -1, 3, None, 0, P, None) == ERR_SHAPE        # negative window
+    assert sel(ctypes.byref(d), 2, -3, None, 0, P, None) == ERR_SHAPE        # negative dilation
+    assert sel(ctypes.byref(d), 0, 0, None, 0, P, None) == ERR_SHAPE         # selects nothing
+    assert sel(ctypes.byref(d), 2, 3, P, 0, P, None) == ERR_SHAPE            # k_in out of range
+    assert sel(ctypes.byref(d), 2, 3, P, 1025, P, None) == ERR_SHAPE
+    assert sel(ctypes.byref(d), 2, 3, None, 0, ctypes.c_void_p(4096 + 4), None) == ERR_ALIGN
+    # width bound: N = 8 blocks; window 2 + ceil(6/3) far + 5 cache entries = 9 -> min(8, 9) = 8
+    assert msa.pattern_width(1024, 2, 3, 5) == 8
+    d7 = _dims(msa, T=1024, topk=7)
+    assert sel(ctypes.byref(d7), 2, 3, P, 5, P, None) == ERR_SHAPE
+    assert msa.pattern_width(1024, 2, 3, 0) == 4
+    d3 = _dims(msa, T=1024, topk=3)
+    assert sel(ctypes.byref(d3), 2, 3, None, 0, P, None) == ERR_SHAPE
