@@ -18,8 +18,8 @@
 // XOR-swizzled on 16-byte chunks (v_mfma_f32_32x32x16_bf16 operands by 16-byte
 // reads and by ds_read_b64_tr_b16 transpose reads).
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
-// token's partials.  dK/dV are added into fp32 accumulators once per item.
-// Nothing is accumulated with atomics.
+// token's partials.  dK/dV are added into fp32 accumulators once per item
+// (atomically only when a block's list is cut into several items).
 #include "msa_common.h"
 #include "msa_internal.h"
 
@@ -298,7 +298,19 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     }
 
     // ---- dK, dV of the owned keys: lane holds head-dim column 32c + l32, keys 32kq + 8j + 4h + i.
-    // Per head-dim tile, all 32 accumulator reads are issued before the stores.
+    if (it.w) {  // one of several items of this block: they run concurrently, so add atomically
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
+          const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
+          unsafeAtomicAdd(&dk_acc[off], dka[c][e]);
+          unsafeAtomicAdd(&dv_acc[off], dva[c][e]);
+        }
+      return;
+    }
+    // The block's only item: per head-dim tile, all 32 accumulator reads are issued before the stores.
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       float ok[16], ov[16];

@@ -48,8 +48,9 @@ __global__ __launch_bounds__(256) void k_inv_colscan(int32_t* __restrict__ count
 }
 
 // One workgroup per (batch, group): exclusive scan of list lengths -> base,
-// and the work items {block, start, len} that cut each list into pieces of at
-// most item_tokens pairs, in block order.
+// and the work items {block, start, len, split} that cut each list into pieces
+// of at most item_tokens pairs, in block order (split = 1 when a block's list
+// spans several items).
 __global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restrict__ len, int32_t* __restrict__ base,
                                                         int4* __restrict__ items, int32_t* __restrict__ item_count,
                                                         int N, int max_items, int item_tokens) {
@@ -84,7 +85,8 @@ __global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restric
     if (blk >= N) break;
     const int l = L[blk];
     base[(size_t)bg * N + blk] = run_l;
-    for (int s = 0; s < l; s += item_tokens) it[run_i++] = make_int4(blk, run_l + s, min(item_tokens, l - s), 0);
+    const int split = l > item_tokens ? 1 : 0;  // .w: the block's list is cut into several items
+    for (int s = 0; s < l; s += item_tokens) it[run_i++] = make_int4(blk, run_l + s, min(item_tokens, l - s), split);
     run_l += l;
   }
 }

@@ -70,3 +70,24 @@ def test_main_branch_on_pattern_cache(msa, oracle_mod):
     for name, got, ref in (("o", o, o_ref), ("lse", lse, lse_ref), ("dq", dq, dq_ref), ("dk", dk, dk_ref),
                            ("dv", dv, dv_ref)):
         parity.assert_close(name, got.cpu(), ref, COS)
+
+
+def test_backward_splits_popular_blocks(msa, oracle_mod):
+    """A block read by more tokens than one backward work item holds is cut into
+    several items whose dK/dV meet in the same accumulator.  Window 1 with
+    dilation 32 makes blocks 0, 32, 64, ... readers of nearly every later token
+    (up to 15104 pairs each), beside diagonal blocks read by 128 tokens only."""
+    cfg = synth.custom(1, 15104, 2, 1, 128, 64, 1)
+    print("split backward items", cfg, flush=True)
+    x = synth.make_inputs(cfg, seed_offset=11)
+    dev = {n: t.cuda() for n, t in x.items()}
+    idx = msa.msa_pattern_select(cfg.B, cfg.T, cfg.G, 1, 32)
+    o, lse = msa.msa_fwd(dev["q"], dev["k"], dev["v"], idx)
+    dq, dk, dv = msa.msa_bwd(dev["q"], dev["k"], dev["v"], o, dev["dout"], lse, idx)
+    torch.cuda.synchronize()
+    dm = Dims(cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, idx.shape[3])
+    idx_h = idx.cpu().numpy()
+    assert (idx_h[0, 0, :, 0] == 0).all()
+    dq_ref, dk_ref, dv_ref = oracle_mod.bwd(dm, x["q"], x["k"], x["v"], x["dout"], idx_h)
+    for name, got, ref in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        parity.assert_close(name, got.cpu(), ref, COS)
