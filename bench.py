@@ -12,10 +12,12 @@ workload (the 128K configuration: B=1, T=131072, 32 query / 4 KV heads, head
 dim 128, 4 proxy heads of dim 64, top-k 32).  Extra fields give the fwd+bwd
 rate with cached indices, effective TFLOP/s on the executed sparse FLOPs,
 per-phase and per-kernel times (HIP events recorded by the library on the
-launch stream), the roofline of the dominant kernel, the 1M configuration as
-a second workload, and the CPU oracle timed on a bounded sample.
+launch stream), the roofline of the dominant kernel, extra workloads (the 1M
+configuration; the 128K step on a fixed window/dilation pattern united with
+the proxy top-k; decode steps of 16 sequences at 128K cached tokens), and the
+CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern|''] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern,decode|''] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -150,6 +152,33 @@ def gpu_inputs(cfg: synth.Config, seed: int = 0) -> dict:
     return out
 
 
+def gpu_decode_inputs(cfg: synth.Config, B: int, seed: int = 0) -> dict:
+    """Decode-step inputs drawn on the GPU with the synth recipe: caches kp
+    [B,T,G,dp] (plus the per-block proxy-key mean), k, v [B,T,G,d], and the new
+    tokens' qp [B,G,dp] and q [B,H,d]."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    shapes = {"k": (B, cfg.T, cfg.G, cfg.d), "v": (B, cfg.T, cfg.G, cfg.d), "kp": (B, cfg.T, cfg.G, cfg.dp),
+              "qp": (B, cfg.G, cfg.dp), "q": (B, cfg.H, cfg.d)}
+    out = {}
+    for i, (name, shp) in enumerate(shapes.items()):
+        g.manual_seed(0x5EED + 104729 * (i + 1) + seed)
+        t = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+        flat = t.view(-1)
+        step = 1 << 26
+        for s in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - s)
+            flat[s:s + n] = torch.randn(n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        out[name] = t
+    g.manual_seed(0x5EED + 104729 * 6 + seed)
+    mu = torch.randn((B, cfg.N, cfg.G, cfg.dp), generator=g, device=dev) * math.sqrt(0.5)
+    for b in range(B):
+        kb = out["kp"][b].float().view(cfg.N, synth.BLOCK, cfg.G, cfg.dp) + mu[b][:, None]
+        out["kp"][b] = kb.view(cfg.T, cfg.G, cfg.dp).to(torch.bfloat16)
+    del mu
+    return out
+
+
 PATTERN = (8, 64)  # window blocks, dilation: the fixed-pattern leg (united with the proxy top-k)
 
 
@@ -234,6 +263,62 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
     return res
 
 
+DECODE_BATCH = 16  # sequences per decode step, each at the workload's full context
+
+
+def run_decode(cfg: synth.Config, B: int, steps: int, warmup: int) -> dict:
+    """One decode step = msa_decode_select + msa_decode_fwd for B sequences whose
+    caches hold cfg.T tokens (the new one last)."""
+    x = gpu_decode_inputs(cfg, B)
+    lens = torch.full((B,), cfg.T, dtype=torch.int32, device="cuda")
+    dims = (B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    ws = msa.Workspace(nbytes=max(msa.msa_workspace_bytes(*dims, op)
+                                  for op in (msa.OP_DECODE_SELECT, msa.OP_DECODE_FWD)))
+    idx = torch.empty((B, cfg.G, cfg.topk), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, cfg.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        msa.msa_decode_select(x["qp"], x["kp"], lens, cfg.topk, ws=ws, out=idx)
+        msa.msa_decode_fwd(x["q"], x["k"], x["v"], lens, idx, ws=ws, out=(o, lse))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    msa.timing_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    kern = {k: v for k, v in msa.timing_read().items() if v[1]}
+    msa.timing_enable(False)
+    # algorithmic HBM bytes per launch: the causal proxy-key cache rows (pool) and
+    # the selected K/V blocks (attention); queries and outputs are noise
+    pool_bytes = float(B) * cfg.T * cfg.G * cfg.dp * 2
+    attn_bytes = float(B) * cfg.G * min(cfg.topk, cfg.N) * 128 * cfg.d * 2 * 2
+    rl = {}
+    for name, work in (("dec_pool", pool_bytes), ("dec_attn", attn_bytes)):
+        ms, n = kern[name]
+        avg_s = ms / n / 1e3
+        rl[name] = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": work / avg_s / 1e9 / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": avg_s * 1e3,
+                    "work_per_launch": work}
+    res = {
+        "workload": "%s decode: B=%d sequences at %d cached tokens" % (cfg.name, B, cfg.T),
+        "shape": {"B": B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk},
+        "ms_per_step": ms_step,
+        "tokens_per_s": B / (ms_step / 1e3),
+        "kernels_ms_per_step": {k: v[0] / steps for k, v in kern.items()},
+        "roofline": rl,
+    }
+    del x, ws, idx, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int) -> dict:
     """Roofline entry of the kernel with the largest time: algorithmic work per
     launch divided by its average launch duration."""
@@ -306,9 +391,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--also", default="1m,pattern",
-                    help="comma list of extra workloads: config names, or 'pattern' (the main config with the fixed "
-                         "window/dilation pattern united with the proxy top-k); '' for none")
+    ap.add_argument("--also", default="1m,pattern,decode",
+                    help="comma list of extra workloads: config names, 'pattern' (the main config with the fixed "
+                         "window/dilation pattern united with the proxy top-k), 'decode' (decode steps of %d "
+                         "sequences at the main config's full context); '' for none" % DECODE_BATCH)
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -347,6 +433,11 @@ def main() -> int:
             print("bench: extra workload %s + pattern %s" % (cfg, PATTERN), file=sys.stderr, flush=True)
             extra.append(run_workload(cfg, args.steps, 2, host_inputs=False, pattern=PATTERN))
             print("bench: pattern done: %.1f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
+            continue
+        if name == "decode":
+            print("bench: decode steps, %d sequences of %s" % (DECODE_BATCH, cfg), file=sys.stderr, flush=True)
+            extra.append(run_decode(cfg, DECODE_BATCH, max(20, 5 * args.steps), 5))
+            print("bench: decode done: %.3f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
             continue
         c = synth.CONFIGS[name]
         print("bench: extra workload %s" % (c,), file=sys.stderr, flush=True)

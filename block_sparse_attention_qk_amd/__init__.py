@@ -12,8 +12,12 @@ Entry points (same names as the C ABI):
   msa_proxy_select(qp, kp, topk)               -> idx            (Index Branch)
   msa_fwd(q, k, v, idx, scale=0.0)             -> (o, lse)       (Main Branch forward)
   msa_bwd(q, k, v, o, dout, lse, idx, scale)   -> (dq, dk, dv)   (Main Branch backward)
+  msa_pattern_select(B, T, G, window, dilation, idx_in) -> idx   (fixed block pattern)
+  msa_decode_select(qp, kp, lens, topk)        -> idx            (decode step, Index Branch)
+  msa_decode_fwd(q, k, v, lens, idx, scale)    -> (o, lse)       (decode step, Main Branch)
 Layouts: qp, kp [B,T,G,dp] bf16; q, o, dout [B,T,H,d] bf16; k, v [B,T,G,d] bf16;
-idx [B,G,T,topk] int32; lse [B,T,H] fp32.
+idx [B,G,T,topk] int32; lse [B,T,H] fp32.  Decode: qp [B,G,dp], q and o [B,H,d],
+caches kp/k/v [B,T,G,*], lens [B] int32 (on the device), idx [B,G,topk], lse [B,H].
 """
 from __future__ import annotations
 
@@ -25,7 +29,8 @@ import torch
 
 __all__ = [
     "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
-    "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "OP_SELECT", "OP_FWD", "OP_BWD", "EXPORTED_SYMBOLS",
+    "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "msa_decode_select",
+    "msa_decode_fwd", "OP_SELECT", "OP_FWD", "OP_BWD", "OP_DECODE_SELECT", "OP_DECODE_FWD", "EXPORTED_SYMBOLS",
     "KERNEL_NAMES", "timing_enable", "timing_read",
 ]
 
@@ -33,14 +38,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmsa.so")
 _lib = None
 
-OP_SELECT, OP_FWD, OP_BWD = 0, 1, 2
+OP_SELECT, OP_FWD, OP_BWD, OP_DECODE_SELECT, OP_DECODE_FWD = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_pattern_select",
-                    "msa_fwd", "msa_bwd", "msa_status_str", "msa_version", "msa_timing_enable",
-                    "msa_timing_read")
+                    "msa_fwd", "msa_bwd", "msa_decode_select", "msa_decode_fwd", "msa_status_str", "msa_version",
+                    "msa_timing_enable", "msa_timing_read")
 
 # msa_kernel_id values (include/msa.h)
 KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
-                "dq_combine", "convert", "pattern")
+                "dq_combine", "convert", "pattern", "dec_pool", "dec_topk", "dec_attn", "dec_combine")
 
 
 class MsaError(RuntimeError):
@@ -74,7 +79,9 @@ def load():
     lib.msa_pattern_select.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
     lib.msa_fwd.argtypes = [D, P, P, P, P, P, P, P, SZ, P]
     lib.msa_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
-    for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd"):
+    lib.msa_decode_select.argtypes = [D, P, P, P, P, P, SZ, P]
+    lib.msa_decode_fwd.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
+    for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd", "msa_decode_select", "msa_decode_fwd"):
         getattr(lib, f).restype = I
     lib.msa_status_str.argtypes = [I]
     lib.msa_status_str.restype = ctypes.c_char_p
@@ -271,3 +278,68 @@ def msa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, 
     _check(lib.msa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(idx),
                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def _lens(lens: torch.Tensor, B: int, device) -> None:
+    _need(lens, "lens", torch.int32, 1)
+    if lens.shape[0] != B:
+        raise ValueError("lens must hold B = %d entries, got %d" % (B, lens.shape[0]))
+    if lens.device != device:
+        raise ValueError("lens must be on %s" % device)
+
+
+def msa_decode_select(qp: torch.Tensor, kp: torch.Tensor, lens: torch.Tensor, topk: int,
+                      ws: Optional[Workspace] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode-step Index Branch: qp [B,G,dp] (the new tokens), kp cache [B,T,G,dp],
+    lens [B] int32 (cached tokens incl. the new one) -> idx [B,G,topk] int32."""
+    _need(qp, "qp", torch.bfloat16, 3)
+    _need(kp, "kp", torch.bfloat16, 4)
+    B, G, dp = qp.shape
+    if kp.shape[0] != B or kp.shape[2] != G or kp.shape[3] != dp:
+        raise ValueError("kp shape %s does not match qp shape %s" % (tuple(kp.shape), tuple(qp.shape)))
+    T = kp.shape[1]
+    _lens(lens, B, qp.device)
+    dims = _dims(B, T, G, G, 64, dp, topk, 0.0)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_SELECT)
+    if nbytes == 0:
+        _check(2)
+    idx = out if out is not None else torch.empty((B, G, topk), dtype=torch.int32, device=qp.device)
+    _need(idx, "idx", torch.int32, 3)
+    w = _ws(ws, qp.device, nbytes)
+    _check(lib.msa_decode_select(ctypes.byref(dims), _ptr(qp), _ptr(kp), _ptr(lens), _ptr(idx), _ptr(w), w.numel(),
+                                 _stream(qp.device)))
+    return idx
+
+
+def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, idx: torch.Tensor,
+                   scale: float = 0.0, ws: Optional[Workspace] = None,
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Decode-step Main Branch: q [B,H,d] (the new tokens), k/v caches [B,T,G,d],
+    lens [B] int32, idx [B,G,topk] -> (o [B,H,d] bf16, lse [B,H] fp32)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(idx, "idx", torch.int32, 3)
+    B, H, d = q.shape
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v shapes %s, %s do not match q shape %s" % (tuple(k.shape), tuple(v.shape),
+                                                                       tuple(q.shape)))
+    T, G = k.shape[1], k.shape[2]
+    if idx.shape[0] != B or idx.shape[1] != G:
+        raise ValueError("idx shape %s does not match [B,G,topk] = [%d,%d,*]" % (tuple(idx.shape), B, G))
+    _lens(lens, B, q.device)
+    dims = _dims(B, T, H, G, d, 32, idx.shape[2], scale)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_FWD)
+    if nbytes == 0:
+        _check(2)
+    if out is None:
+        o = torch.empty((B, H, d), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    w = _ws(ws, q.device, nbytes)
+    _check(lib.msa_decode_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(idx), _ptr(o),
+                              _ptr(lse), _ptr(w), w.numel(), _stream(q.device)))
+    return o, lse

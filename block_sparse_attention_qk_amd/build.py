@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmsa.so")
 
-SOURCES = ["msa_api.hip", "msa_select.hip", "msa_pattern.hip", "msa_inverse.hip", "msa_fwd.hip", "msa_bwd.hip"]
+SOURCES = ["msa_api.hip", "msa_select.hip", "msa_pattern.hip", "msa_inverse.hip", "msa_fwd.hip", "msa_bwd.hip",
+           "msa_decode.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -61,6 +61,11 @@ Layout layout(const Geo& g, msa_op op, int W) {
   const size_t pairs = BG * (size_t)W * g.K;
   if (op == MSA_OP_SELECT) {
     L.pooled = c.take(BG * (size_t)W * g.N * 4);
+  } else if (op == MSA_OP_DECODE_SELECT) {
+    L.pooled = c.take(BG * (size_t)g.N * 4);
+  } else if (op == MSA_OP_DECODE_FWD) {
+    L.part_o = c.take(BG * (size_t)g.K * g.R * g.D * 4);
+    L.part_lse = c.take(BG * (size_t)g.K * g.R * 4);
   } else if (op == MSA_OP_FWD) {
     carve_inverse(L, c, g, W, FWD_ITEM_TOKENS);
     L.part_o = c.take((pairs + 1) * g.R * g.D * 2);  // + a spare slot for rows past an item's list
@@ -112,6 +117,16 @@ msa_status make_geo(const msa_dims* d, msa_op op, Geo* g) {
     if (!is_pow2_le16(g->R) || (d->d != 64 && d->d != 128)) return MSA_ERR_UNSUPPORTED;
   }
   g->scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)g->D);
+  return MSA_OK;
+}
+
+bool is_decode(msa_op op) { return op == MSA_OP_DECODE_SELECT || op == MSA_OP_DECODE_FWD; }
+
+// Decode geometry: the training checks plus a grid bound on B*G (grid y).
+msa_status make_dec_geo(const msa_dims* d, msa_op op, Geo* g) {
+  const msa_status s = make_geo(d, op == MSA_OP_DECODE_SELECT ? MSA_OP_SELECT : MSA_OP_FWD, g);
+  if (s != MSA_OK) return s;
+  if ((int64_t)d->B * d->G > 65535) return MSA_ERR_SHAPE;
   return MSA_OK;
 }
 
@@ -179,6 +194,8 @@ extern "C" {
 
 size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
   Geo g;
+  if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return 0;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
   const size_t full = layout(g, op, g.T).total;
   const size_t cap = op == MSA_OP_SELECT ? CAP_SELECT : CAP_MAIN;
@@ -189,6 +206,8 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
 
 size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op) {
   Geo g;
+  if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return 0;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
   return layout(g, op, min_window(g)).total;
 }
@@ -293,6 +312,42 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   }
   MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dk_acc, dk, kv, st));
   MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dv_acc, dv, kv, st));
+  return MSA_OK;
+}
+
+msa_status msa_decode_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp, const int32_t* len,
+                             int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  const msa_status s = make_dec_geo(dims, MSA_OP_DECODE_SELECT, &g);
+  if (s != MSA_OK) return s;
+  if (!qp || !kp || !len || !idx || !ws) return MSA_ERR_NULL;
+  if (!al16(qp) || !al16(kp) || !al16(len) || !al16(idx) || !al16(ws)) return MSA_ERR_ALIGN;
+  const Layout L = layout(g, MSA_OP_DECODE_SELECT, 0);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* pooled = reinterpret_cast<float*>(static_cast<char*>(ws) + L.pooled);
+  MSA_LAUNCH(MSA_K_DEC_POOL, st, launch_dec_pool(g, qp, kp, len, pooled, st));
+  MSA_LAUNCH(MSA_K_DEC_TOPK, st, launch_dec_topk(g, pooled, len, idx, st));
+  return MSA_OK;
+}
+
+msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                          const int32_t* len, const int32_t* idx, msa_bf16* o, float* lse, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Geo g;
+  const msa_status s = make_dec_geo(dims, MSA_OP_DECODE_FWD, &g);
+  if (s != MSA_OK) return s;
+  if (!q || !k || !v || !len || !idx || !o || !lse || !ws) return MSA_ERR_NULL;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(len) || !al16(idx) || !al16(o) || !al16(lse) || !al16(ws))
+    return MSA_ERR_ALIGN;
+  const Layout L = layout(g, MSA_OP_DECODE_FWD, 0);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* part_o = reinterpret_cast<float*>(base + L.part_o);
+  float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  MSA_LAUNCH(MSA_K_DEC_ATTN, st, launch_dec_attn(g, q, k, v, len, idx, part_o, part_lse, st));
+  MSA_LAUNCH(MSA_K_DEC_COMBINE, st, launch_dec_combine(g, part_o, part_lse, idx, len, o, lse, st));
   return MSA_OK;
 }
 

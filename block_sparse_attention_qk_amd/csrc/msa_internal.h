@@ -30,7 +30,7 @@ struct InvBufs {
   int32_t* counts;      // [BG][nchunk][N]
   int32_t* base;        // [BG][N]   list start of each block
   int32_t* len;         // [BG][N]   list length of each block
-  int4* items;          // [BG][max_items]  {block, start, len, 0}
+  int4* items;          // [BG][max_items]  {block, start, len, split}
   int32_t* item_count;  // [BG]
   int32_t* list;        // [BG][W * K]  pair ids (t - t0) * K + slot
   int max_items;
@@ -57,5 +57,14 @@ hipError_t launch_dq_combine(const Geo& g, const Win& w, const int32_t* idx, con
 hipError_t launch_cvt_bf16(const float* src, uint16_t* dst, size_t n, hipStream_t st);
 hipError_t launch_pattern(const int32_t* idx_in, int k_in, int32_t* idx_out, int K, int B, int G, int T,
                           int window, int dilation, hipStream_t st);
+
+// ---- Decode step (one new query per sequence; caches [B, T, G, *])
+hipError_t launch_dec_pool(const Geo& g, const uint16_t* qp, const uint16_t* kp, const int32_t* len, float* pooled,
+                           hipStream_t st);
+hipError_t launch_dec_topk(const Geo& g, const float* pooled, const int32_t* len, int32_t* idx, hipStream_t st);
+hipError_t launch_dec_attn(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* len,
+                           const int32_t* idx, float* part_o, float* part_lse, hipStream_t st);
+hipError_t launch_dec_combine(const Geo& g, const float* part_o, const float* part_lse, const int32_t* idx,
+                              const int32_t* len, uint16_t* o, float* lse, hipStream_t st);
 
 }  // namespace msa

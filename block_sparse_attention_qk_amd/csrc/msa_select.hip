@@ -10,6 +10,7 @@
 
 #include "msa_common.h"
 #include "msa_internal.h"
+#include "msa_topk.h"
 
 namespace msa {
 
@@ -155,145 +156,15 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
-// Top-k of one pooled row per wavefront.  Scores become order-preserving u32
-// keys held in registers (VPL per lane).  The k-th largest key is found by a
-// three-digit radix select (11, 11 and 10 bits): each digit is histogrammed in
-// LDS over the keys that match the digits found so far, and a wave scan from
-// the top bin finds the bin where the count of larger keys reaches k.  Blocks
-// above the k-th key are taken, then blocks equal to it lowest index first;
-// a ballot pass writes the chosen block ids in ascending order, and the row
-// tail is -1.
-constexpr int TOPK_BINS = 2048;
-
 template <int VPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, int32_t* __restrict__ idx,
                                               int T, int N, int K, int t0, int W, int rows) {
   __shared__ uint32_t hist_all[4][TOPK_BINS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t* hist = hist_all[wave];
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;  // whole wave exits: no block-level barrier below
   const int bg = row / W, tl = row % W, t = t0 + tl;
-  const int nc = t / BLK + 1;
-  const int nsel = min(K, nc);
-  const float* pr = pooled + (size_t)row * N;
-
-  uint32_t key[VPL];
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int col = i * 64 + lane;
-    uint32_t kk = 0;
-    if (col < nc) {
-      float f = pr[col];
-      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
-      const uint32_t u = __float_as_uint(f);
-      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    key[i] = kk;
-  }
-
-  uint32_t prefix = 0;
-  int need = nsel;  // rank of the wanted key among keys matching prefix
-  if constexpr (VPL <= 16) {
-    // Short rows: build the k-th largest key bit by bit from the top; each
-    // step is one ballot count per register of keys.
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i * 64 < nc) cnt += __popcll(__ballot((i * 64 + lane < nc) && key[i] >= cand));
-      if (cnt >= nsel) prefix = cand;
-    }
-    int cnt_gt = 0;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (i * 64 < nc) cnt_gt += __popcll(__ballot((i * 64 + lane < nc) && key[i] > prefix));
-    need = nsel - cnt_gt;
-  } else {
-  // Radix select of the nsel-th largest key.  Pooled scores of a row share
-  // their sign and exponent bits, so the digits start below the common prefix
-  // of the row's smallest and largest key (otherwise every key would fall into
-  // one histogram bin).
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i * 64 >= nc) break;
-    if (i * 64 + lane < nc) {
-      kmin = min(kmin, key[i]);
-      kmax = max(kmax, key[i]);
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
-  const uint32_t diff = kmin ^ kmax;
-  int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // low bits still undecided
-  prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
-  while (bits > 0) {
-    const int width = bits < 11 ? bits : 11;
-    const int sh = bits - width, nbins = 1 << width;
-    const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
-    for (int j = lane; j < nbins; j += 64) hist[j] = 0;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (i * 64 >= nc) break;
-      if (i * 64 + lane < nc && (key[i] & hi_mask) == prefix)
-        atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // lanes own `per` consecutive bins each, scanned from the top bin down
-    const int per = nbins >= 64 ? nbins / 64 : 1;
-    const int top = nbins - per * lane;
-    uint32_t lsum = 0;
-    if (top > 0)
-      for (int j = 0; j < per; ++j) lsum += hist[top - 1 - j];
-    uint32_t incl = lsum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const uint32_t excl = incl - lsum;
-    const unsigned long long hit = __ballot(top > 0 && excl < (uint32_t)need && (uint32_t)need <= incl);
-    const int owner = __builtin_ctzll(hit);
-    uint32_t run = __shfl(excl, owner);
-    const int otop = nbins - per * owner;
-    int bin = otop - 1;
-    for (int j = 0; j < per; ++j) {  // every lane walks the owner's bins (LDS broadcast)
-      const uint32_t c = hist[otop - 1 - j];
-      if (run + c >= (uint32_t)need) { bin = otop - 1 - j; break; }
-      run += c;
-    }
-    need -= (int)run;
-    prefix |= (uint32_t)bin << sh;
-    bits = sh;
-    __builtin_amdgcn_wave_barrier();
-  }
-  }
-  const uint32_t kth = prefix;
-  const int need_eq = need;  // equal keys to take, lowest block index first
-
-  int32_t* out = idx + ((size_t)bg * T + t) * K;
-  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int run_eq = 0, run_sel = 0;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i * 64 >= nc) break;
-    const bool valid = i * 64 + lane < nc;
-    const bool eq = valid && key[i] == kth, gt = valid && key[i] > kth;
-    const unsigned long long meq = __ballot(eq);
-    const int rank = run_eq + __popcll(meq & lt);
-    const bool sel = gt || (eq && rank < need_eq);
-    const unsigned long long msel = __ballot(sel);
-    if (sel) out[run_sel + __popcll(msel & lt)] = i * 64 + lane;
-    run_eq += __popcll(meq);
-    run_sel += __popcll(msel);
-  }
-  for (int p = nsel + lane; p < K; p += 64) out[p] = -1;
+  topk_row<VPL>(pooled + (size_t)row * N, t / BLK + 1, K, idx + ((size_t)bg * T + t) * K, hist_all[wave], lane);
 }
 
 hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,

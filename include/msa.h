@@ -81,7 +81,13 @@ typedef struct {
   float scale; /* softmax scale; <= 0 selects 1/sqrt(d) */
 } msa_dims;
 
-typedef enum { MSA_OP_SELECT = 0, MSA_OP_FWD = 1, MSA_OP_BWD = 2 } msa_op;
+typedef enum {
+  MSA_OP_SELECT = 0,
+  MSA_OP_FWD = 1,
+  MSA_OP_BWD = 2,
+  MSA_OP_DECODE_SELECT = 3, /* msa_decode_select: B*G*(T/128) fp32 pooled scores */
+  MSA_OP_DECODE_FWD = 4     /* msa_decode_fwd: B*G*topk fp32 partials of R*(d+1) values */
+} msa_op;
 
 /* Workspace that lets `op` process all tokens in one window (capped at a
  * few tens of GiB for the largest shapes, which are then walked in windows).
@@ -145,6 +151,43 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
                    msa_bf16* dq, msa_bf16* dk, msa_bf16* dv, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* ---- Decode step: one new query per sequence against its caches.
+ * ai-beat "flash-msa-sparse-attention-training", paragraph 1: MSA also serves
+ * inference (prefill and decode).  Prefill is msa_proxy_select + msa_fwd on
+ * the prompt.  A decode step computes for the new token of each sequence what
+ * those two compute for its row: with t = len[b] - 1 the new token's position,
+ * its own key, value and proxy key already written at position t of the caches.
+ *
+ * Layouts (device pointers, contiguous, 16-byte aligned):
+ *   qp  [B, G, dp]  bf16    proxy query of the new token
+ *   q   [B, H, d]   bf16    query heads of the new token; o the same shape
+ *   kp  [B, T, G, dp], k, v [B, T, G, d]  bf16 caches of capacity T tokens
+ *   len [B]         int32   tokens cached per sequence, the new one included
+ *   idx [B, G, topk] int32  block-index row of the new token
+ *   lse [B, H]      fp32
+ * dims: B, T (cache capacity; T % 128 == 0), H, G, d, dp, topk and scale as
+ * for the training entry points (msa_decode_select reads B, T, G, dp, topk).
+ * len values are read on the device: a sequence whose len is outside 1..T gets
+ * an all -1 idx row, o = 0 and lse = -inf.  Cache rows at or past len are never
+ * read.  ws must hold msa_workspace_bytes(dims, MSA_OP_DECODE_SELECT or
+ * MSA_OP_DECODE_FWD) bytes (the minimum is the same). */
+
+/* For every (b, g): pooled_i = max over cached keys j <= t of block i of
+ * dot(qp[b,g,:], kp[b,j,g,:]) (fp32), i <= t/128; the min(topk, t/128 + 1)
+ * highest blocks (ties: lower index) ascending in idx[b,g,:], -1 after. */
+msa_status msa_decode_select(const msa_dims* dims, const msa_bf16* qp, const msa_bf16* kp, const int32_t* len,
+                             int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* For every (b, h), g = h / (H/G), over J = { j <= t : j/128 listed in
+ * idx[b,g,:] } and s_j = scale * q[b,h,:].k[b,j,g,:]:
+ *   o[b,h,:] = sum_j softmax(s)_j v[b,j,g,:] (bf16),  lse[b,h] = ln sum_j exp(s_j).
+ * idx entries that are -1 or above t/128 are ignored; a row with no other
+ * entry gives o = 0, lse = -inf.  Blocks listed twice are counted twice, so
+ * rows should be as msa_decode_select writes them. */
+msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                          const int32_t* len, const int32_t* idx, msa_bf16* o, float* lse, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* ---- Optional launch timing, for benchmarks and profiling tools.
  * When enabled, the library records a pair of HIP events on the call's stream
  * around every launch of the kernels listed below (the inverse-index build
@@ -164,7 +207,11 @@ typedef enum {
   MSA_K_DQ_COMBINE = 7,   /* dQ partial sums */
   MSA_K_CONVERT = 8,      /* fp32 -> bf16 of dK, dV */
   MSA_K_PATTERN = 9,      /* fixed window/dilation pattern (msa_pattern_select) */
-  MSA_K_COUNT = 10
+  MSA_K_DEC_POOL = 10,    /* decode: proxy scores of the new query + block max-pool */
+  MSA_K_DEC_TOPK = 11,    /* decode: top-k of each (sequence, group) row */
+  MSA_K_DEC_ATTN = 12,    /* decode: per-slot attention partials */
+  MSA_K_DEC_COMBINE = 13, /* decode: log-sum-exp merge of the slots */
+  MSA_K_COUNT = 14
 } msa_kernel_id;
 
 /* on != 0 enables timing; any call clears what was recorded. */

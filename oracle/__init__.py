@@ -238,3 +238,72 @@ def pattern_select(B: int, T: int, G: int, window: int, dilation: int, width: in
                     raise ValueError("pattern row of %d blocks exceeds width %d" % (len(row), width))
                 out[b, g, t, :len(row)] = row
     return out
+
+
+def _decode_len(lens, B: int, T: int) -> np.ndarray:
+    ln = np.asarray(lens, dtype=np.int64).reshape(-1)
+    if ln.size != B:
+        raise ValueError("lens must hold B = %d entries" % B)
+    return ln
+
+
+def decode_select(dm: Dims, qp, kp, lens):
+    """Index Branch of a decode step (ai-beat "flash-msa-sparse-attention-training",
+    paragraph 1: MSA also serves inference).  Sequence b has lens[b] cached
+    tokens, the new one last, at t = lens[b] - 1; its proxy query qp[b] ([B,G,dp])
+    is row t of the sequence whose proxy keys are kp[b, :t+1] ([B,T,G,dp] cache
+    of capacity dm.T).  The row is selected exactly as a training row (select()
+    on that prefix).  Returns (idx [B,G,topk] int32, pooled [B,G,T/128] fp32,
+    -inf past the causal blocks); sequences with lens outside 1..T give an all -1
+    row and -inf scores."""
+    qp64, kp64 = _f64(qp), _f64(kp)
+    ln = _decode_len(lens, dm.B, dm.T)
+    N = (dm.T + BLOCK - 1) // BLOCK
+    idx = np.full((dm.B, dm.G, dm.topk), -1, dtype=np.int32)
+    pooled = np.full((dm.B, dm.G, N), -np.inf, dtype=np.float32)
+    for b in range(dm.B):
+        L = int(ln[b])
+        if L < 1 or L > dm.T:
+            continue
+        qrow = np.zeros((1, L, dm.G, dm.dp), dtype=np.float64)
+        qrow[0, L - 1] = qp64[b]
+        ib, pb = select(Dims(1, L, dm.H, dm.G, dm.d, dm.dp, dm.topk, dm.scale), qrow, kp64[b:b + 1, :L],
+                        rows=[L - 1], return_pooled=True)
+        idx[b] = ib[0]
+        pooled[b, :, :pb.shape[2]] = pb[0]
+    return idx, pooled
+
+
+def decode_fwd(dm: Dims, q, k, v, lens, idx):
+    """Main Branch of a decode step: for sequence b the new query heads q[b]
+    ([B,H,d]) are row t = lens[b] - 1 of the sequence whose keys and values are
+    k[b, :t+1], v[b, :t+1] ([B,T,G,d] caches), attending over the blocks of
+    idx[b] ([B,G,topk]) exactly as fwd() does for a training row (one call per
+    group).  Entries that are -1 or above t/128 are dropped first.  Returns
+    (o [B,H,d], lse [B,H]) in float64; a group whose row keeps no entry, or a
+    sequence with lens outside 1..T, gives o = 0, lse = -inf."""
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    ix = _i32(idx)
+    ln = _decode_len(lens, dm.B, dm.T)
+    R = dm.H // dm.G
+    o = np.zeros((dm.B, dm.H, dm.d), dtype=np.float64)
+    lse = np.full((dm.B, dm.H), -np.inf, dtype=np.float64)
+    for b in range(dm.B):
+        L = int(ln[b])
+        if L < 1 or L > dm.T:
+            continue
+        t = L - 1
+        for g in range(dm.G):
+            ent = sorted(int(e) for e in ix[b, g] if 0 <= e <= t // BLOCK)
+            if not ent:
+                continue
+            row = np.full((1, 1, L, dm.topk), -1, dtype=np.int32)
+            row[0, 0, t, :len(ent)] = ent
+            qg = np.zeros((1, L, R, dm.d), dtype=np.float64)
+            qg[0, t] = q64[b, g * R:(g + 1) * R]
+            og, lg = fwd(Dims(1, L, R, 1, dm.d, dm.dp, dm.topk, dm.scale), qg,
+                         np.ascontiguousarray(k64[b:b + 1, :L, g:g + 1]),
+                         np.ascontiguousarray(v64[b:b + 1, :L, g:g + 1]), row, rows=[t])
+            o[b, g * R:(g + 1) * R] = og[0]
+            lse[b, g * R:(g + 1) * R] = lg[0]
+    return o, lse

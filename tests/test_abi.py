@@ -186,3 +186,37 @@ def test_pattern_select_checks(lib, msa):
     assert msa.pattern_width(1024, 2, 3, 0) == 4
     d3 = _dims(msa, T=1024, topk=3)
     assert sel(ctypes.byref(d3), 2, 3, None, 0, P, None) == ERR_SHAPE
+
+
+def test_decode_checks(lib, msa):
+    P, Q = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    d = _dims(msa, B=2, T=1024, topk=8)
+    sel, fwd = lib.msa_decode_select, lib.msa_decode_fwd
+    need_s = lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_DECODE_SELECT)
+    need_f = lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_DECODE_FWD)
+    assert need_s >= 2 * 2 * 8 * 4                      # B*G*N fp32 pooled scores
+    assert need_f >= 2 * 2 * 8 * 4 * (128 + 1) * 4      # B*G*topk partials of R*(d+1) fp32
+    assert lib.msa_workspace_min_bytes(ctypes.byref(d), msa.OP_DECODE_FWD) == need_f
+    assert lib.msa_workspace_bytes(ctypes.byref(d), 5) == 0          # no such op
+    assert sel(None, P, P, P, P, P, need_s, None) == ERR_NULL
+    for i in range(5):
+        args = [P] * 5
+        args[i] = None
+        assert sel(ctypes.byref(d), *args, need_s, None) == ERR_NULL, i
+        args[i] = Q
+        assert sel(ctypes.byref(d), *args, need_s, None) == ERR_ALIGN, i
+    for i in range(8):
+        args = [P] * 8
+        args[i] = None
+        assert fwd(ctypes.byref(d), *args, need_f, None) == ERR_NULL, i
+        args[i] = Q
+        assert fwd(ctypes.byref(d), *args, need_f, None) == ERR_ALIGN, i
+    assert sel(ctypes.byref(d), P, P, P, P, P, need_s - 1, None) == ERR_WS
+    assert fwd(ctypes.byref(d), P, P, P, P, P, P, P, P, need_f - 1, None) == ERR_WS
+    for kw, code in ((dict(T=1000), ERR_SHAPE), (dict(dp=48), ERR_UNSUP), (dict(topk=0), ERR_SHAPE),
+                     (dict(B=40000, G=2), ERR_SHAPE)):
+        bad = _dims(msa, **kw)
+        assert sel(ctypes.byref(bad), P, P, P, P, P, 1 << 40, None) == code, kw
+    for kw, code in ((dict(H=6, G=2), ERR_UNSUP), (dict(d=96), ERR_UNSUP), (dict(H=6, G=4), ERR_SHAPE)):
+        bad = _dims(msa, **kw)
+        assert fwd(ctypes.byref(bad), P, P, P, P, P, P, P, P, 1 << 40, None) == code, kw

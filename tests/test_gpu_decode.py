@@ -1,0 +1,120 @@
+"""Decode step (one new query per sequence) on the GPU through the C ABI
+against the oracle: block indices bit-exact up to near-ties, o and lse to the
+main parity bar with the GPU's indices shared, out-of-range lengths, and the
+decode rows against the training path's rows of the same sequences."""
+import numpy as np
+import pytest
+import torch
+
+import parity
+import synth
+from oracle import Dims
+
+pytestmark = pytest.mark.gpu
+
+COS = 0.999
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_attention_qk_amd as m
+    m.load()
+    return m
+
+
+CASES = [
+    # B, T, H, G, d, dp, topk, lens (cached tokens incl. the new one)
+    (4, 2048, 8, 2, 128, 64, 4, [2048, 1, 129, 1000]),      # G*dp = 128: 2 groups per wave load
+    (3, 1024, 4, 1, 64, 32, 16, [1024, 128, 700]),          # topk above the block count
+    (2, 4096, 32, 4, 128, 64, 8, [4096, 3001]),             # 128K-config heads (R = 8)
+    (2, 2048, 16, 1, 128, 128, 3, [2048, 1500]),            # R = 16, dp = 128
+    (2, 1024, 2, 2, 64, 64, 2, [1024, 77]),                 # R = 1
+    (2, 1024, 16, 16, 64, 32, 2, [1024, 513]),              # 16 groups in one wave load
+    (1, 8192, 4, 1, 64, 32, 64, [8192]),                    # 64 blocks, ballot top-k
+]
+
+
+def _decode_case(msa, oracle_mod, cfg, lens, seed=0):
+    x = synth.make_inputs(cfg, seed_offset=seed)
+    B = cfg.B
+    rows = [min(max(L, 1), cfg.T) - 1 for L in lens]
+    qp = torch.stack([x["qp"][b, rows[b]] for b in range(B)])
+    q = torch.stack([x["q"][b, rows[b]] for b in range(B)])
+    dev = {n: x[n].cuda() for n in ("kp", "k", "v")}
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx = msa.msa_decode_select(qp.cuda(), dev["kp"], lens_d, cfg.topk)
+    o, lse = msa.msa_decode_fwd(q.cuda(), dev["k"], dev["v"], lens_d, idx)
+    torch.cuda.synchronize()
+    dm = Dims(B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    idx_h = idx.cpu().numpy()
+    idx_ref, pooled = oracle_mod.decode_select(dm, qp, x["kp"], lens)
+    valid = [b for b in range(B) if 1 <= lens[b] <= cfg.T]
+    for b in range(B):
+        if b not in valid:
+            assert (idx_h[b] == -1).all()
+    info = parity.check_indices(idx_h[valid], idx_ref[valid], pooled[valid], cfg.topk)
+    o_ref, lse_ref = oracle_mod.decode_fwd(dm, q, x["k"], x["v"], lens, idx_h)
+    res = [info, parity.assert_close("o", o.cpu()[valid], o_ref[valid], COS),
+           parity.assert_close("lse", lse.cpu()[valid], lse_ref[valid], COS)]
+    for b in range(B):
+        if b not in valid:
+            assert (o[b] == 0).all() and torch.isneginf(lse[b]).all()
+    print(res, flush=True)
+    return x, idx, o, lse
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dT%dH%dG%dd%ddp%dk%d" % c[:7])
+def test_decode_matches_oracle(msa, oracle_mod, case):
+    B, T, H, G, d, dp, topk, lens = case
+    print("decode case", case, flush=True)
+    _decode_case(msa, oracle_mod, synth.custom(B, T, H, G, d, dp, topk), lens, seed=31)
+
+
+def test_out_of_range_lengths(msa, oracle_mod):
+    print("decode lengths 0 and T+1", flush=True)
+    _decode_case(msa, oracle_mod, synth.custom(3, 1024, 8, 2, 64, 32, 4), [0, 1025, 600], seed=32)
+
+
+def test_decode_rows_equal_training_rows(msa, oracle_mod):
+    """A decode step over a sequence's caches gives that sequence's training row."""
+    cfg = synth.custom(2, 4096, 32, 4, 128, 64, 8)
+    lens = [4096, 2222]
+    print("decode vs training rows", cfg, flush=True)
+    x, idx, o, lse = _decode_case(msa, oracle_mod, cfg, lens, seed=33)
+    dev = {n: t.cuda() for n, t in x.items()}
+    idx_t = msa.msa_proxy_select(dev["qp"], dev["kp"], cfg.topk)
+    o_t, lse_t = msa.msa_fwd(dev["q"], dev["k"], dev["v"], idx_t)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        assert torch.equal(idx[b].cpu(), idx_t[b, :, L - 1].cpu()), b
+        parity.assert_close("o_vs_train", o[b].cpu(), o_t[b, L - 1].cpu(), 0.99999, 2 ** -7)
+        parity.assert_close("lse_vs_train", lse[b].cpu(), lse_t[b, L - 1].cpu(), 0.99999, 1e-4)
+
+
+def _full_size_check(msa, oracle_mod, cfg, B, lens):
+    import bench
+    print("full-size decode", cfg.name, B, lens, flush=True)
+    x = bench.gpu_decode_inputs(cfg, B, seed=5)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx = msa.msa_decode_select(x["qp"], x["kp"], lens_d, cfg.topk)
+    o, lse = msa.msa_decode_fwd(x["q"], x["k"], x["v"], lens_d, idx)
+    torch.cuda.synchronize()
+    dm = Dims(B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    idx_h = idx.cpu().numpy()
+    idx_ref, pooled = oracle_mod.decode_select(dm, x["qp"].cpu(), x["kp"].cpu(), lens)
+    print("indices", parity.check_indices(idx_h, idx_ref, pooled, cfg.topk), flush=True)
+    o_ref, lse_ref = oracle_mod.decode_fwd(dm, x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), lens, idx_h)
+    print(parity.assert_close("o", o.cpu(), o_ref, COS), parity.assert_close("lse", lse.cpu(), lse_ref, COS),
+          flush=True)
+
+
+def test_128k_config_decode(msa, oracle_mod):
+    cfg = synth.CONFIGS["128k"]
+    _full_size_check(msa, oracle_mod, cfg, 2, [cfg.T, 100003])
+
+
+def test_1m_config_decode(msa, oracle_mod):
+    cfg = synth.CONFIGS["1m"]
+    _full_size_check(msa, oracle_mod, cfg, 1, [cfg.T - 5])
