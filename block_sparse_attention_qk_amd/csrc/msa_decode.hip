@@ -93,23 +93,159 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_pool(const bf16raw* __re
   if (tok == 0 && c % CPG == 0) pooled[((size_t)b * G + g0 + gg) * N + blk] = m;
 }
 
-// Top-k of each (sequence, group) pooled row: the same rule as the training
-// rows (min(K, t/128 + 1) blocks, ascending, -1 tail).  Sequences whose length
-// is outside 1..T get an all -1 row.
-template <int VPL>
-__global__ __launch_bounds__(256) void k_dec_topk(const float* __restrict__ pooled, const int32_t* __restrict__ len,
-                                                  int32_t* __restrict__ idx, int T, int G, int N, int K, int rows) {
-  __shared__ uint32_t hist_all[4][TOPK_BINS];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= rows) return;  // whole wave exits: no block-level barrier below
+// Top-k of each (sequence, group) pooled row with the rule of the training
+// rows (min(K, t/128 + 1) blocks, ties to the lower index, ascending, -1 tail),
+// one 1024-thread workgroup per row: decode has few rows, so the whole
+// workgroup shares one row.  Thread i holds the order-preserving keys of
+// blocks i, i + 1024, ...; the k-th largest key comes from a radix select over
+// digits of the bits below the row's common prefix (histograms in LDS, the bin
+// found by one wave's scan); the chosen blocks are then written in ascending
+// order by a workgroup prefix count.  Sequences whose length is outside 1..T
+// get an all -1 row.
+constexpr int DTK_THREADS = 1024;
+constexpr int DTK_WAVES = DTK_THREADS / 64;
+
+template <int VPT>
+__global__ __launch_bounds__(DTK_THREADS) void k_dec_topk(const float* __restrict__ pooled,
+                                                          const int32_t* __restrict__ len, int32_t* __restrict__ idx,
+                                                          int T, int G, int N, int K) {
+  __shared__ uint32_t hist[TOPK_BINS];
+  __shared__ uint32_t red[2][DTK_WAVES];
+  __shared__ int bc[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
   const int L = len[row / G];
   int32_t* out = idx + (size_t)row * K;
   if (L < 1 || L > T) {
-    for (int p = lane; p < K; p += 64) out[p] = -1;
-    return;
+    for (int p = tid; p < K; p += DTK_THREADS) out[p] = -1;
+    return;  // whole workgroup
   }
-  topk_row<VPL>(pooled + (size_t)row * N, (L - 1) / BLK + 1, K, out, hist_all[wave], lane);
+  const int nc = (L - 1) / BLK + 1, nsel = min(K, nc);
+  const float* pr = pooled + (size_t)row * N;
+  uint32_t key[VPT];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int col = i * DTK_THREADS + tid;
+    uint32_t kk = 0;
+    if (col < nc) {
+      float f = pr[col];
+      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
+      const uint32_t u = __float_as_uint(f);
+      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
+    }
+    key[i] = kk;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < DTK_WAVES; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  // Radix select of the nsel-th largest key below the common prefix of kmin and kmax.
+  const uint32_t diff = kmin ^ kmax;
+  int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);
+  uint32_t prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
+  int need = nsel;  // rank of the wanted key among the keys matching prefix
+  while (bits > 0) {
+    const int width = bits < 11 ? bits : 11;
+    const int sh = bits - width, nbins = 1 << width;
+    const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
+    for (int j = tid; j < nbins; j += DTK_THREADS) hist[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (i * DTK_THREADS + tid < nc && (key[i] & hi_mask) == prefix) atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lanes own `per` consecutive bins each, scanned from the top bin down
+      const int per = nbins >= 64 ? nbins / 64 : 1;
+      const int top = nbins - per * lane;
+      uint32_t lsum = 0;
+      if (top > 0)
+        for (int j = 0; j < per; ++j) lsum += hist[top - 1 - j];
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const uint32_t excl = incl - lsum;
+      const unsigned long long hit = __ballot(top > 0 && excl < (uint32_t)need && (uint32_t)need <= incl);
+      const int owner = __builtin_ctzll(hit);
+      uint32_t run = __shfl(excl, owner);
+      const int otop = nbins - per * owner;
+      int bin = otop - 1;
+      for (int j = 0; j < per; ++j) {
+        const uint32_t c = hist[otop - 1 - j];
+        if (run + c >= (uint32_t)need) {
+          bin = otop - 1 - j;
+          break;
+        }
+        run += c;
+      }
+      if (lane == 0) {
+        bc[0] = bin;
+        bc[1] = need - (int)run;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << sh;
+    need = bc[1];
+    bits = sh;
+    __syncthreads();  // bc and hist are rewritten by the next digit
+  }
+  const uint32_t kth = prefix;
+  const int need_eq = need;  // keys equal to kth to take, lowest block index first
+  // Ascending write-out: blocks in column order i * 1024 + tid, ranks from
+  // per-wave ballots and a prefix over the waves.
+  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base_eq = 0, base_sel = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int col = i * DTK_THREADS + tid;
+    const bool valid = col < nc;
+    const bool eq = valid && key[i] == kth, gt = valid && key[i] > kth;
+    const unsigned long long meq = __ballot(eq);
+    if (lane == 0) red[0][wave] = (uint32_t)__popcll(meq);
+    __syncthreads();
+    int eq_before = base_eq, eq_total = 0;
+#pragma unroll
+    for (int w = 0; w < DTK_WAVES; ++w) {
+      const int c = (int)red[0][w];
+      if (w < wave) eq_before += c;
+      eq_total += c;
+    }
+    const bool sel = gt || (eq && eq_before + __popcll(meq & lt) < need_eq);
+    const unsigned long long msel = __ballot(sel);
+    if (lane == 0) red[1][wave] = (uint32_t)__popcll(msel);
+    __syncthreads();
+    int sel_before = base_sel, sel_total = 0;
+#pragma unroll
+    for (int w = 0; w < DTK_WAVES; ++w) {
+      const int c = (int)red[1][w];
+      if (w < wave) sel_before += c;
+      sel_total += c;
+    }
+    if (sel) out[sel_before + __popcll(msel & lt)] = col;
+    base_eq += eq_total;
+    base_sel += sel_total;
+    __syncthreads();  // red is rewritten by the next column group
+  }
+  for (int p = nsel + tid; p < K; p += DTK_THREADS) out[p] = -1;
 }
 
 // Attention of the new query's R heads over one selected block (one workgroup
@@ -158,6 +294,17 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_attn(const bf16raw* __re
     ka[st] = ld8(krow + 16 * st);
     qb[st] = ld8(qrow + 16 * st);
   }
+  // Value rows for P V (lane: two columns c0, c0 + 1 of keys kbase + i*KH + kh), issued
+  // together with the K rows so that both HBM round trips overlap.
+  const int c0 = 2 * (lane % (D / 2));
+  const int kh = lane / (D / 2);  // 0 for d = 128
+  uint32_t vv[32 / KH];
+#pragma unroll
+  for (int i = 0; i < 32 / KH; ++i) {
+    const int key = min(kbase + i * KH + kh, t);
+    vv[i] = *reinterpret_cast<const uint32_t*>(v + (((size_t)b * T + key) * G + g) * D + c0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 acc = zero16();
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
@@ -192,17 +339,9 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_attn(const bf16raw* __re
   __builtin_amdgcn_wave_barrier();
 
   // ---- P V over the wave's 32 keys
-  const int c0 = 2 * (lane % (D / 2));
-  const int kh = lane / (D / 2);  // 0 for d = 128
   float o0[R], o1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) o0[r] = o1[r] = 0.f;
-  uint32_t vv[32 / KH];
-#pragma unroll
-  for (int i = 0; i < 32 / KH; ++i) {
-    const int key = min(kbase + i * KH + kh, t);
-    vv[i] = *reinterpret_cast<const uint32_t*>(v + (((size_t)b * T + key) * G + g) * D + c0);
-  }
 #pragma unroll
   for (int i = 0; i < 32 / KH; ++i) {
     const float v0 = bf_lo(vv[i]), v1 = bf_hi(vv[i]);
@@ -246,44 +385,74 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_attn(const bf16raw* __re
   }
 }
 
-// Log-sum-exp merge of a (sequence, group)'s slot partials into o (bf16) and
-// lse (natural log).  Rows with no valid slot (length outside 1..T) get o = 0
-// and lse = -inf.
-template <int D, int R>
-__global__ __launch_bounds__(256) void k_dec_combine(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_lse,
-                                                     const int32_t* __restrict__ idx,
-                                                     const int32_t* __restrict__ len, bf16raw* __restrict__ o,
-                                                     float* __restrict__ lse, int T, int G, int K) {
-  const int bg = blockIdx.x, b = bg / G, g = bg % G;
+// Log-sum-exp merge of the slot partials of one (sequence, head): NW waves
+// per head (4, or 16 for long rows), wave w taking slots w, w + NW, ...  The
+// workgroup first finds the
+// max of the valid slots' lse, then every lane adds the weighted partials of
+// its D/64 value columns over its wave's slots (the loads do not depend on each
+// other), and the NW sums meet in LDS.  Rows with no valid slot (length
+// outside 1..T) get o = 0 and lse = -inf.
+template <int D, int R, int DCB_WAVES>
+__global__ __launch_bounds__(64 * DCB_WAVES) void k_dec_combine(const float* __restrict__ part_o,
+                                                                const float* __restrict__ part_lse,
+                                                                const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ len,
+                                                                bf16raw* __restrict__ o, float* __restrict__ lse,
+                                                                int T, int G, int K) {
+  constexpr int CL = D / 64;  // value columns per lane
+  __shared__ float red[DCB_WAVES];
+  __shared__ float acc[DCB_WAVES][D + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.x, H = G * R, b = bh / H, h = bh % H, g = h / R, hh = h % R;
+  const int bg = b * G + g;
   const int L = len[b];
   const int nb = (L >= 1 && L <= T) ? (L - 1) / BLK + 1 : 0;  // causal blocks; 0 = no valid slot
   const int32_t* row = idx + (size_t)bg * K;
-  const int H = G * R;
-  for (int x = threadIdx.x; x < R * D; x += 256) {
-    const int hh = x / D, cc = x % D;
-    float M = -INFINITY, sw = 0.f, so = 0.f;
-    for (int sl = 0; sl < K; ++sl) {
-      const int blk = row[sl];
-      if (blk < 0 || blk >= nb) continue;
-      const size_t p = (size_t)bg * K + sl;
-      const float ls = part_lse[p * R + hh];
-      const float val = part_o[p * R * D + x];
-      if (ls > M) {
-        const float f = M == -INFINITY ? 0.f : __expf(M - ls);
-        sw *= f;
-        so *= f;
-        M = ls;
-      }
-      const float w = __expf(ls - M);
-      sw += w;
-      so = fmaf(w, val, so);
-    }
-    const size_t oh = (size_t)b * H + g * R + hh;
-    const float out = M == -INFINITY ? 0.f : so / sw;
-    o[oh * D + cc] = f2bf(out);
-    if (cc == 0) lse[oh] = M == -INFINITY ? -INFINITY : M + __logf(sw);
+  const float* pl = part_lse + (size_t)bg * K * R + hh;
+  const float* po = part_o + ((size_t)bg * K * R + hh) * D + CL * lane;
+  float M = -INFINITY;
+  for (int sl = threadIdx.x; sl < K; sl += 64 * DCB_WAVES) {
+    const int blk = row[sl];
+    if (blk >= 0 && blk < nb) M = fmaxf(M, pl[(size_t)sl * R]);
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < DCB_WAVES; ++w) M = fmaxf(M, red[w]);
+  float sw = 0.f, so[CL];
+#pragma unroll
+  for (int c = 0; c < CL; ++c) so[c] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int sl = wave; sl < K; sl += DCB_WAVES) {
+      const int blk = row[sl];
+      const bool ok = blk >= 0 && blk < nb;
+      const float w = ok ? __expf(pl[(size_t)sl * R] - M) : 0.f;
+      sw += w;
+      const float* src = po + (size_t)sl * R * D;
+#pragma unroll
+      for (int c = 0; c < CL; ++c) so[c] = fmaf(w, ok ? src[c] : 0.f, so[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CL; ++c) acc[wave][CL * lane + c] = so[c];
+  if (lane == 0) acc[wave][D] = sw;
+  __syncthreads();
+  if (wave != 0) return;
+  float tw = 0.f;
+#pragma unroll
+  for (int w = 0; w < DCB_WAVES; ++w) tw += acc[w][D];
+  const size_t oh = (size_t)b * H + h;
+#pragma unroll
+  for (int c = 0; c < CL; ++c) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < DCB_WAVES; ++w) v += acc[w][CL * lane + c];
+    o[oh * D + CL * lane + c] = f2bf(M == -INFINITY ? 0.f : v / tw);
+  }
+  if (lane == 0) lse[oh] = M == -INFINITY ? -INFINITY : M + __logf(tw);
 }
 
 // ---- host launchers
@@ -312,21 +481,16 @@ hipError_t launch_dec_pool(const Geo& g, const uint16_t* qp, const uint16_t* kp,
 
 hipError_t launch_dec_topk(const Geo& g, const float* pooled, const int32_t* len, int32_t* idx, hipStream_t st) {
   const int rows = g.B * g.G;
-  dim3 grid((rows + 3) / 4), block(256);
-  const int need = (g.N + 63) / 64;
-#define MSA_DEC_TOPK(V)                                                                    \
-  if (need <= V) {                                                                         \
-    k_dec_topk<V><<<grid, block, 0, st>>>(pooled, len, idx, g.T, g.G, g.N, g.K, rows);     \
-    return hipGetLastError();                                                              \
+  const int need = (g.N + DTK_THREADS - 1) / DTK_THREADS;
+#define MSA_DEC_TOPK(V)                                                                       \
+  if (need <= V) {                                                                            \
+    k_dec_topk<V><<<dim3(rows), dim3(DTK_THREADS), 0, st>>>(pooled, len, idx, g.T, g.G, g.N, g.K); \
+    return hipGetLastError();                                                                 \
   }
   MSA_DEC_TOPK(1)
   MSA_DEC_TOPK(2)
   MSA_DEC_TOPK(4)
   MSA_DEC_TOPK(8)
-  MSA_DEC_TOPK(16)
-  MSA_DEC_TOPK(32)
-  MSA_DEC_TOPK(64)
-  MSA_DEC_TOPK(128)
 #undef MSA_DEC_TOPK
   return hipErrorInvalidValue;
 }
@@ -348,11 +512,15 @@ hipError_t launch_dec_attn(const Geo& g, const uint16_t* q, const uint16_t* k, c
 
 hipError_t launch_dec_combine(const Geo& g, const float* part_o, const float* part_lse, const int32_t* idx,
                               const int32_t* len, uint16_t* o, float* lse, hipStream_t st) {
-  dim3 grid(g.B * g.G), block(256);
-#define MSA_DEC_COMB(DV, RV)                                                                             \
-  if (g.D == DV && g.R == RV) {                                                                          \
-    k_dec_combine<DV, RV><<<grid, block, 0, st>>>(part_o, part_lse, idx, len, o, lse, g.T, g.G, g.K);    \
-    return hipGetLastError();                                                                            \
+  const bool wide = g.K >= 128;  // long rows: 16 waves share a head's slots
+  dim3 grid(g.B * g.H), block(wide ? 1024 : 256);
+#define MSA_DEC_COMB(DV, RV)                                                                                     \
+  if (g.D == DV && g.R == RV) {                                                                                  \
+    if (wide)                                                                                                    \
+      k_dec_combine<DV, RV, 16><<<grid, block, 0, st>>>(part_o, part_lse, idx, len, o, lse, g.T, g.G, g.K);     \
+    else                                                                                                         \
+      k_dec_combine<DV, RV, 4><<<grid, block, 0, st>>>(part_o, part_lse, idx, len, o, lse, g.T, g.G, g.K);      \
+    return hipGetLastError();                                                                                    \
   }
   MSA_DEC_COMB(64, 1) MSA_DEC_COMB(64, 2) MSA_DEC_COMB(64, 4) MSA_DEC_COMB(64, 8) MSA_DEC_COMB(64, 16)
   MSA_DEC_COMB(128, 1) MSA_DEC_COMB(128, 2) MSA_DEC_COMB(128, 4) MSA_DEC_COMB(128, 8) MSA_DEC_COMB(128, 16)

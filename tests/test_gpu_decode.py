@@ -32,7 +32,9 @@ CASES = [
     (2, 2048, 16, 1, 128, 128, 3, [2048, 1500]),            # R = 16, dp = 128
     (2, 1024, 2, 2, 64, 64, 2, [1024, 77]),                 # R = 1
     (2, 1024, 16, 16, 64, 32, 2, [1024, 513]),              # 16 groups in one wave load
-    (1, 8192, 4, 1, 64, 32, 64, [8192]),                    # 64 blocks, ballot top-k
+    (1, 8192, 4, 1, 64, 32, 64, [8192]),                    # 64 blocks
+    (1, 262144, 2, 1, 64, 32, 40, [262144 - 77]),           # 2048 blocks: two keys per top-k thread
+    (2, 524288, 2, 1, 64, 32, 160, [524288, 300000]),       # 4096 blocks: four keys per top-k thread; wide combine
 ]
 
 
@@ -75,6 +77,25 @@ def test_decode_matches_oracle(msa, oracle_mod, case):
 def test_out_of_range_lengths(msa, oracle_mod):
     print("decode lengths 0 and T+1", flush=True)
     _decode_case(msa, oracle_mod, synth.custom(3, 1024, 8, 2, 64, 32, 4), [0, 1025, 600], seed=32)
+
+
+@pytest.mark.parametrize("T,topk", [(2048, 5), (1 << 20, 300)])
+def test_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
+    """A proxy-key cache that repeats one 128-row block gives every complete
+    block the same pooled score: the lowest block ids must win, on both sides."""
+    print("decode ties", T, topk, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(7)
+    base = torch.randn((128, G, dp), generator=g).to(torch.bfloat16)
+    kp = base.repeat(T // 128, 1, 1).unsqueeze(0).contiguous()
+    qp = torch.randn((1, G, dp), generator=g).to(torch.bfloat16)
+    lens = [T - 3]
+    idx = msa.msa_decode_select(qp.cuda(), kp.cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"), topk)
+    torch.cuda.synchronize()
+    dm = Dims(1, T, 1, G, 64, dp, topk)
+    idx_ref, _ = oracle_mod.decode_select(dm, qp, kp, lens)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    assert list(idx_ref[0, 0]) == list(range(topk))
 
 
 def test_decode_rows_equal_training_rows(msa, oracle_mod):
