@@ -401,6 +401,9 @@ def main() -> int:
                     help="also run one plain device copy of this many MiB (reference kernel for traffic counters)")
     ap.add_argument("--gpu-inputs", action="store_true",
                     help="draw the main workload's inputs on the GPU (same recipe, different stream; for profiling)")
+    ap.add_argument("--decode-only", metavar="CONFIG",
+                    help="run only decode steps (%d sequences at CONFIG's full context) and print their record; "
+                         "for profiling" % DECODE_BATCH)
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="print calibrated per-kernel HBM bytes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR "
                          "(needs --copy-calibration-mib of those runs) and exit; no GPU needed")
@@ -423,6 +426,10 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.decode_only:
+        res = run_decode(synth.CONFIGS[args.decode_only], DECODE_BATCH, max(20, 5 * args.steps), 5)
+        print(json.dumps(res))
+        return 0
     cfg = synth.CONFIGS[args.config]
     print("bench: %s steps=%d warmup=%d" % (cfg, args.steps, args.warmup), file=sys.stderr, flush=True)
     main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=not args.gpu_inputs)
