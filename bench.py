@@ -14,10 +14,11 @@ rate with cached indices, effective TFLOP/s on the executed sparse FLOPs,
 per-phase and per-kernel times (HIP events recorded by the library on the
 launch stream), the roofline of the dominant kernel, extra workloads (the 1M
 configuration; the 128K step on a fixed window/dilation pattern united with
-the proxy top-k; decode steps of 16 sequences at 128K cached tokens), and the
+the proxy top-k; the 128K step through the merged forward/backward call;
+decode steps of 16 sequences at 128K cached tokens), and the
 CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern,decode|''] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern,merged,decode|''] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -182,16 +183,19 @@ def gpu_decode_inputs(cfg: synth.Config, B: int, seed: int = 0) -> dict:
 PATTERN = (8, 64)  # window blocks, dilation: the fixed-pattern leg (united with the proxy top-k)
 
 
-def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, pattern=None) -> dict:
+def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, pattern=None,
+                 merged: bool = False) -> dict:
     """One step = proxy select (+ the fixed window/dilation pattern united with
-    it, when `pattern` is given) + forward + backward over the cache."""
+    it, when `pattern` is given) + forward + backward over the cache (one
+    msa_fwd_bwd call when `merged`)."""
     if host_inputs:
         x = {n: t.cuda() for n, t in synth.make_inputs(cfg).items()}
     else:
         x = gpu_inputs(cfg)
     width = msa.pattern_width(cfg.T, pattern[0], pattern[1], cfg.topk) if pattern else cfg.topk
     dims = (cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, width)
-    ws_bytes = max(msa.msa_workspace_bytes(*dims, op) for op in (msa.OP_SELECT, msa.OP_FWD, msa.OP_BWD))
+    ops = (msa.OP_SELECT, msa.OP_FWD_BWD) if merged else (msa.OP_SELECT, msa.OP_FWD, msa.OP_BWD)
+    ws_bytes = max(msa.msa_workspace_bytes(*dims, op) for op in ops)
     ws = msa.Workspace(nbytes=ws_bytes)
     idx = torch.empty((cfg.B, cfg.G, cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
     idx_main = torch.empty((cfg.B, cfg.G, cfg.T, width), dtype=torch.int32, device="cuda") if pattern else idx
@@ -207,10 +211,15 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
                                    out=idx_main)
         if ev:
             ev[1].record()
-        msa.msa_fwd(x["q"], x["k"], x["v"], idx_main, ws=ws, out=(o, lse))
-        if ev:
-            ev[2].record()
-        msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx_main, ws=ws, out=(dq, dk, dv))
+        if merged:
+            msa.msa_fwd_bwd(x["q"], x["k"], x["v"], x["dout"], idx_main, ws=ws, out=(o, lse, dq, dk, dv))
+            if ev:
+                ev[2].record()
+        else:
+            msa.msa_fwd(x["q"], x["k"], x["v"], idx_main, ws=ws, out=(o, lse))
+            if ev:
+                ev[2].record()
+            msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx_main, ws=ws, out=(dq, dk, dv))
         if ev:
             ev[3].record()
 
@@ -241,13 +250,15 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
     f_pair = 4 * cfg.d * cfg.R * 128  # forward flop per (token, group, block); backward is 2.5x
     f_fwd, f_bwd, f_proxy = f_pair * pairs, 2.5 * f_pair * pairs, cfg.flops_proxy()
     res = {
-        "workload": cfg.name + ("+pattern(window=%d,dilation=%d)" % pattern if pattern else ""),
+        "workload": cfg.name + ("+pattern(window=%d,dilation=%d)" % pattern if pattern else "") +
+                    (" merged fwd+bwd (msa_fwd_bwd)" if merged else ""),
         "shape": {"B": cfg.B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk,
                   "cache_width": width},
         "ms_per_step": ms_step,
         "wall_ms_per_step": 1e3 * wall / steps,
         "tokens_per_s": tokens / (ms_step / 1e3),
-        "phases_ms": {"select": t_sel, "fwd": t_fwd, "bwd": t_bwd},
+        "phases_ms": {"select": t_sel, "fwd": t_fwd, "bwd": t_bwd} if not merged else {"select": t_sel,
+                                                                                          "fwd_bwd": t_fwd + t_bwd},
         "fwd_bwd_tokens_per_s": tokens / ((t_fwd + t_bwd) / 1e3),
         "fwd_bwd_effective_tflops": (f_fwd + f_bwd) / ((t_fwd + t_bwd) / 1e3) / 1e12,
         "select_tflops": f_proxy / (t_sel / 1e3) / 1e12,
@@ -391,10 +402,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--also", default="1m,pattern,decode",
+    ap.add_argument("--also", default="1m,pattern,merged,decode",
                     help="comma list of extra workloads: config names, 'pattern' (the main config with the fixed "
-                         "window/dilation pattern united with the proxy top-k), 'decode' (decode steps of %d "
-                         "sequences at the main config's full context); '' for none" % DECODE_BATCH)
+                         "window/dilation pattern united with the proxy top-k), 'merged' (the main config through "
+                         "msa_fwd_bwd), 'decode' (decode steps of %d sequences at the main config's full context); "
+                         "'' for none" % DECODE_BATCH)
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -440,6 +452,11 @@ def main() -> int:
             print("bench: extra workload %s + pattern %s" % (cfg, PATTERN), file=sys.stderr, flush=True)
             extra.append(run_workload(cfg, args.steps, 2, host_inputs=False, pattern=PATTERN))
             print("bench: pattern done: %.1f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
+            continue
+        if name == "merged":
+            print("bench: extra workload %s, merged fwd+bwd" % (cfg,), file=sys.stderr, flush=True)
+            extra.append(run_workload(cfg, args.steps, 2, host_inputs=False, merged=True))
+            print("bench: merged done: %.1f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
             continue
         if name == "decode":
             print("bench: decode steps, %d sequences of %s" % (DECODE_BATCH, cfg), file=sys.stderr, flush=True)

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   msa_proxy_select(qp, kp, topk)               -> idx            (Index Branch)
   msa_fwd(q, k, v, idx, scale=0.0)             -> (o, lse)       (Main Branch forward)
   msa_bwd(q, k, v, o, dout, lse, idx, scale)   -> (dq, dk, dv)   (Main Branch backward)
+  msa_fwd_bwd(q, k, v, dout, idx, scale)       -> (o, lse, dq, dk, dv)  (merged forward + backward)
   msa_pattern_select(B, T, G, window, dilation, idx_in) -> idx   (fixed block pattern)
   msa_decode_select(qp, kp, lens, topk)        -> idx            (decode step, Index Branch)
   msa_decode_fwd(q, k, v, lens, idx, scale)    -> (o, lse)       (decode step, Main Branch)
@@ -29,8 +30,9 @@ import torch
 
 __all__ = [
     "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
-    "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "msa_decode_select",
-    "msa_decode_fwd", "OP_SELECT", "OP_FWD", "OP_BWD", "OP_DECODE_SELECT", "OP_DECODE_FWD", "EXPORTED_SYMBOLS",
+    "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "msa_fwd_bwd",
+    "msa_decode_select", "msa_decode_fwd", "OP_SELECT", "OP_FWD", "OP_BWD", "OP_DECODE_SELECT", "OP_DECODE_FWD",
+    "OP_FWD_BWD", "EXPORTED_SYMBOLS",
     "KERNEL_NAMES", "timing_enable", "timing_read",
 ]
 
@@ -38,10 +40,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmsa.so")
 _lib = None
 
-OP_SELECT, OP_FWD, OP_BWD, OP_DECODE_SELECT, OP_DECODE_FWD = 0, 1, 2, 3, 4
+OP_SELECT, OP_FWD, OP_BWD, OP_DECODE_SELECT, OP_DECODE_FWD, OP_FWD_BWD = 0, 1, 2, 3, 4, 5
 EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_pattern_select",
-                    "msa_fwd", "msa_bwd", "msa_decode_select", "msa_decode_fwd", "msa_status_str", "msa_version",
-                    "msa_timing_enable", "msa_timing_read")
+                    "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select", "msa_decode_fwd", "msa_status_str",
+                    "msa_version", "msa_timing_enable", "msa_timing_read")
 
 # msa_kernel_id values (include/msa.h)
 KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
@@ -79,9 +81,11 @@ def load():
     lib.msa_pattern_select.argtypes = [D, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P]
     lib.msa_fwd.argtypes = [D, P, P, P, P, P, P, P, SZ, P]
     lib.msa_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_fwd_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_decode_select.argtypes = [D, P, P, P, P, P, SZ, P]
     lib.msa_decode_fwd.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
-    for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd", "msa_decode_select", "msa_decode_fwd"):
+    for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select",
+              "msa_decode_fwd"):
         getattr(lib, f).restype = I
     lib.msa_status_str.argtypes = [I]
     lib.msa_status_str.restype = ctypes.c_char_p
@@ -278,6 +282,32 @@ def msa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, 
     _check(lib.msa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(idx),
                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def msa_fwd_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, idx: torch.Tensor,
+                scale: float = 0.0, ws: Optional[Workspace] = None, out=None):
+    """Merged forward + backward: (o, lse, dq, dk, dv), as msa_fwd followed by
+    msa_bwd on that o, with one inverse index per window and D fused."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(idx, "idx", torch.int32, 4)
+    if v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("inconsistent shapes for msa_fwd_bwd")
+    dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    lib = load()
+    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_FWD_BWD)
+    if nbytes == 0:
+        _check(2)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        o, lse, dq, dk, dv = out
+    w = _ws(ws, q.device, nbytes)
+    _check(lib.msa_fwd_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(idx), _ptr(o), _ptr(lse),
+                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
+    return o, lse, dq, dk, dv
 
 
 def _lens(lens: torch.Tensor, B: int, device) -> None:

@@ -28,6 +28,8 @@ struct Layout {
   size_t pooled = 0;
   size_t counts = 0, base = 0, len = 0, items = 0, item_count = 0, list = 0;
   int max_items = 0;
+  size_t items2 = 0, item_count2 = 0;  // merged call: backward items cut from the same inverse index
+  int max_items2 = 0;
   size_t part_o = 0, part_lse = 0;
   size_t Dd = 0, dk_acc = 0, dv_acc = 0, dq_part = 0;
 };
@@ -66,6 +68,20 @@ Layout layout(const Geo& g, msa_op op, int W) {
   } else if (op == MSA_OP_DECODE_FWD) {
     L.part_o = c.take(BG * (size_t)g.K * g.R * g.D * 4);
     L.part_lse = c.take(BG * (size_t)g.K * g.R * 4);
+  } else if (op == MSA_OP_FWD_BWD) {
+    // One inverse index serves both halves; the forward partials are dead once
+    // the window's combine has run, so the dQ partials reuse their memory.
+    const size_t kv = (size_t)g.B * g.T * g.G * g.D;
+    L.Dd = c.take((size_t)g.B * g.T * g.H * 4);
+    L.dk_acc = c.take(kv * 4);
+    L.dv_acc = c.take(kv * 4);
+    carve_inverse(L, c, g, W, FWD_ITEM_TOKENS);
+    L.max_items2 = inv_max_items(g, W, BWD_ITEM_TOKENS);
+    L.items2 = c.take(BG * (size_t)L.max_items2 * 16);
+    L.item_count2 = c.take(BG * 4);
+    L.part_lse = c.take((pairs + 1) * g.R * 4);
+    L.part_o = c.take((pairs + 1) * g.R * g.D * 2);
+    L.dq_part = L.part_o;
   } else if (op == MSA_OP_FWD) {
     carve_inverse(L, c, g, W, FWD_ITEM_TOKENS);
     L.part_o = c.take((pairs + 1) * g.R * g.D * 2);  // + a spare slot for rows past an item's list
@@ -195,7 +211,7 @@ extern "C" {
 size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
   Geo g;
   if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
-  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_FWD_BWD) return 0;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
   const size_t full = layout(g, op, g.T).total;
   const size_t cap = op == MSA_OP_SELECT ? CAP_SELECT : CAP_MAIN;
@@ -207,7 +223,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
 size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op) {
   Geo g;
   if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
-  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_FWD_BWD) return 0;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
   return layout(g, op, min_window(g)).total;
 }
@@ -275,7 +291,7 @@ msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
     const Win w{t0, std::min(W, g.T - t0)};
     MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse(g, w, idx, ib, FWD_ITEM_TOKENS, st));
     MSA_LAUNCH(MSA_K_FWD_PARTIALS, st, launch_fwd_partials(g, w, q, k, v, ib, part_o, part_lse, st));
-    MSA_LAUNCH(MSA_K_FWD_COMBINE, st, launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, st));
+    MSA_LAUNCH(MSA_K_FWD_COMBINE, st, launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, nullptr, nullptr, st));
   }
   return MSA_OK;
 }
@@ -308,6 +324,50 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
     const Win w{t0, std::min(W, g.T - t0)};
     MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse(g, w, idx, ib, BWD_ITEM_TOKENS, st));
     MSA_LAUNCH(MSA_K_BWD_PARTIALS, st, launch_bwd_partials(g, w, q, k, v, dout, lse, Dd, ib, dq_part, dk_acc, dv_acc, st));
+    MSA_LAUNCH(MSA_K_DQ_COMBINE, st, launch_dq_combine(g, w, idx, dq_part, dq, st));
+  }
+  MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dk_acc, dk, kv, st));
+  MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dv_acc, dv, kv, st));
+  return MSA_OK;
+}
+
+msa_status msa_fwd_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                       const msa_bf16* dout, const int32_t* idx, msa_bf16* o, float* lse, msa_bf16* dq, msa_bf16* dk,
+                       msa_bf16* dv, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  const msa_status s = make_geo(dims, MSA_OP_FWD_BWD, &g);
+  if (s != MSA_OK) return s;
+  if (!q || !k || !v || !dout || !idx || !o || !lse || !dq || !dk || !dv || !ws) return MSA_ERR_NULL;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(dout) || !al16(idx) || !al16(o) || !al16(lse) || !al16(dq) ||
+      !al16(dk) || !al16(dv) || !al16(ws))
+    return MSA_ERR_ALIGN;
+  const int W = fit_window(g, MSA_OP_FWD_BWD, ws_bytes);
+  if (W == 0) return MSA_ERR_WORKSPACE;
+  const Layout L = layout(g, MSA_OP_FWD_BWD, W);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const InvBufs ib = inv_bufs(L, base);
+  InvBufs ib2 = ib;  // same list, backward-sized items
+  ib2.items = reinterpret_cast<int4*>(base + L.items2);
+  ib2.item_count = reinterpret_cast<int32_t*>(base + L.item_count2);
+  ib2.max_items = L.max_items2;
+  float* Dd = reinterpret_cast<float*>(base + L.Dd);
+  float* dk_acc = reinterpret_cast<float*>(base + L.dk_acc);
+  float* dv_acc = reinterpret_cast<float*>(base + L.dv_acc);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  uint16_t* dq_part = reinterpret_cast<uint16_t*>(base + L.dq_part);
+  const size_t kv = (size_t)g.B * g.T * g.G * g.D;
+  MSA_LAUNCH(MSA_K_BWD_DOT, st, launch_fill_zero(dk_acc, kv, st));
+  MSA_LAUNCH(MSA_K_BWD_DOT, st, launch_fill_zero(dv_acc, kv, st));
+  for (int t0 = 0; t0 < g.T; t0 += W) {
+    const Win w{t0, std::min(W, g.T - t0)};
+    MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse(g, w, idx, ib, FWD_ITEM_TOKENS, st));
+    MSA_LAUNCH(MSA_K_INVERSE, st, launch_inverse_items(g, ib2, BWD_ITEM_TOKENS, st));
+    MSA_LAUNCH(MSA_K_FWD_PARTIALS, st, launch_fwd_partials(g, w, q, k, v, ib, part_o, part_lse, st));
+    MSA_LAUNCH(MSA_K_FWD_COMBINE, st, launch_fwd_combine(g, w, idx, part_o, part_lse, o, lse, dout, Dd, st));
+    MSA_LAUNCH(MSA_K_BWD_PARTIALS, st,
+               launch_bwd_partials(g, w, q, k, v, dout, lse, Dd, ib2, dq_part, dk_acc, dv_acc, st));
     MSA_LAUNCH(MSA_K_DQ_COMBINE, st, launch_dq_combine(g, w, idx, dq_part, dq, st));
   }
   MSA_LAUNCH(MSA_K_CONVERT, st, launch_cvt_bf16(dk_acc, dk, kv, st));

@@ -376,12 +376,24 @@ __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ 
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
   for (int s0 = 0; s0 < K; s0 += SB) {
+    // entries and partial rows of the batch are loaded together; slots past K
+    // re-read the last one and slots without a partial are masked after the load
+    int ent[SB];
     uint4 raw[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int s = s0 + u;
-      const bool ok = s < K && (unsigned)ir[s] <= last;
-      raw[u] = ok ? ld16u(pp + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
+      const int s = min(s0 + u, K - 1);
+      ent[u] = ir[s];
+      raw[u] = ld16u(pp + (size_t)s * R * D);
+    }
+    // keep every load above the masking (the compiler would otherwise sink one
+    // into a branch and issue it after the rest, costing a second round trip)
+#pragma unroll
+    for (int u = 0; u < SB; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const bool ok = s0 + u < K && (unsigned)ent[u] <= last;
+      raw[u] = ok ? raw[u] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < SB; ++u) {

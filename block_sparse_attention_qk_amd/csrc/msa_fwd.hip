@@ -208,11 +208,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
 // group, token) row per R*D/8 threads (each thread owns 8 head-dim values of
 // one head and streams 16 bytes per slot).  A slot holds a partial iff its
 // cache entry is a valid causal block.  A row with no valid entry gets
-// O = 0, LSE = -inf.
-template <int D, int R>
+// O = 0, LSE = -inf.  WITH_D (the merged forward/backward call) also forms the
+// backward's D = rowsum(dout * O) here, while O is still in registers.
+template <int D, int R, bool WITH_D>
 __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__ idx, const bf16raw* __restrict__ part_o,
                                                      const float* __restrict__ part_lse, bf16raw* __restrict__ o,
-                                                     float* __restrict__ lse, int T, int H, int G, int K, int t0,
+                                                     float* __restrict__ lse, const bf16raw* __restrict__ dout,
+                                                     float* __restrict__ Dd, int T, int H, int G, int K, int t0,
                                                      int W, int rows) {
   constexpr int TPR = R * D / 8;  // threads per row
   constexpr int RPB = 256 / TPR;  // rows per block
@@ -226,22 +228,38 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   const unsigned last = (unsigned)(t / BLK);
   const float* pl = part_lse + p0 * R + hh;
   const bf16raw* po = part_o + (p0 * R + hh) * D + c8;
+  const size_t orow = (size_t)(b * T + t) * H + g * R + hh;
+  uint4 dch = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (WITH_D) dch = ld16u(dout + orow * D + c8);  // issued ahead of the slot stream
 
-  // One pass with a running maximum: each batch loads its slots' lse and
-  // partial rows together, and the accumulator is rescaled when the maximum grows.
+  // One pass with a running maximum: each batch loads its slots' cache
+  // entries, lse and partial rows together (slots past K re-read the last one;
+  // a slot without a partial is read and then masked, so no load waits on a
+  // branch), and the accumulator is rescaled when the maximum grows.
   constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
   float M = -INFINITY, L = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < K; s0 += SB) {
+    int ent[SB];
     float lv[SB];
     uint4 raw[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int s = s0 + u;
-      const bool ok = s < K && (unsigned)ir[s] <= last;
-      lv[u] = ok ? pl[(size_t)s * R] : -INFINITY;
-      raw[u] = ok ? ld16u(po + (size_t)s * R * D) : make_uint4(0u, 0u, 0u, 0u);
+      const int s = min(s0 + u, K - 1);
+      ent[u] = ir[s];
+      lv[u] = pl[(size_t)s * R];
+      raw[u] = ld16u(po + (size_t)s * R * D);
+    }
+    // keep every load above the masking (the compiler would otherwise sink one
+    // into a branch and issue it after the rest, costing a second round trip)
+#pragma unroll
+    for (int u = 0; u < SB; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const bool ok = s0 + u < K && (unsigned)ent[u] <= last;
+      lv[u] = ok ? lv[u] : -INFINITY;
+      raw[u] = ok ? raw[u] : make_uint4(0u, 0u, 0u, 0u);
     }
     float mb = M;
 #pragma unroll
@@ -266,10 +284,25 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
     M = mb;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const size_t orow = (size_t)(b * T + t) * H + g * R + hh;
-  st16u(o + orow * D + c8, make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
-                                      pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv)));
+  const uint4 ob = make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
+                              pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv));
+  st16u(o + orow * D + c8, ob);
   if (c8 == 0) lse[orow] = L > 0.f ? M + fast_log2(L) * LN2 : -INFINITY;
+  if constexpr (WITH_D) {
+    // D = rowsum(dout * o) of the bf16 o just written, summed in the order of
+    // k_bwd_dot (8 products per lane, then xor shuffles over the D/8 lanes of
+    // the head), so the merged call reproduces msa_bwd's D bit for bit.
+    const uint32_t aw[4] = {ob.x, ob.y, ob.z, ob.w}, cw[4] = {dch.x, dch.y, dch.z, dch.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += __uint_as_float(aw[i] << 16) * __uint_as_float(cw[i] << 16);
+      s += __uint_as_float(aw[i] & 0xffff0000u) * __uint_as_float(cw[i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int off = D / 16; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (c8 == 0) Dd[orow] = s;
+  }
 }
 
 template <int D, int R>
@@ -284,11 +317,16 @@ static hipError_t fwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, 
 
 template <int D, int R>
 static hipError_t fwd_combine_t(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* part_o,
-                                const float* part_lse, uint16_t* o, float* lse, hipStream_t st) {
+                                const float* part_lse, uint16_t* o, float* lse, const uint16_t* dout, float* Dd,
+                                hipStream_t st) {
   const int rows = g.B * g.G * w.W;
   constexpr int RPB = 256 / (R * D / 8);
-  k_fwd_combine<D, R><<<(rows + RPB - 1) / RPB, 256, 0, st>>>(idx, part_o, part_lse, o, lse, g.T, g.H, g.G, g.K,
-                                                               w.t0, w.W, rows);
+  if (dout != nullptr)
+    k_fwd_combine<D, R, true><<<(rows + RPB - 1) / RPB, 256, 0, st>>>(idx, part_o, part_lse, o, lse, dout, Dd, g.T,
+                                                                      g.H, g.G, g.K, w.t0, w.W, rows);
+  else
+    k_fwd_combine<D, R, false><<<(rows + RPB - 1) / RPB, 256, 0, st>>>(idx, part_o, part_lse, o, lse, nullptr,
+                                                                       nullptr, g.T, g.H, g.G, g.K, w.t0, w.W, rows);
   return hipGetLastError();
 }
 
@@ -313,8 +351,9 @@ hipError_t launch_fwd_partials(const Geo& g, const Win& w, const uint16_t* q, co
 }
 
 hipError_t launch_fwd_combine(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* part_o,
-                              const float* part_lse, uint16_t* o, float* lse, hipStream_t st) {
-  MSA_DISPATCH_DR(fwd_combine_t, g, w, idx, part_o, part_lse, o, lse, st)
+                              const float* part_lse, uint16_t* o, float* lse, const uint16_t* dout, float* Dd,
+                              hipStream_t st) {
+  MSA_DISPATCH_DR(fwd_combine_t, g, w, idx, part_o, part_lse, o, lse, dout, Dd, st)
 }
 
 }  // namespace msa

@@ -38,13 +38,18 @@ struct InvBufs {
 int inv_max_items(const Geo& g, int W, int item_tokens);
 hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const InvBufs& ib,
                           int item_tokens, hipStream_t st);
+// Work items {block, start, len, split} of the inverse index already built in
+// `ib` (counts/len/base/list), cut at another item size into ib's items buffer.
+hipError_t launch_inverse_items(const Geo& g, const InvBufs& ib, int item_tokens, hipStream_t st);
 
 // ---- Main Branch
 hipError_t launch_fwd_partials(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, const InvBufs& ib, uint16_t* part_o,
                                float* part_lse, hipStream_t st);
+// dout/Dd non-null: also D = rowsum(dout * o) into Dd [B, T, H] (merged forward/backward)
 hipError_t launch_fwd_combine(const Geo& g, const Win& w, const int32_t* idx, const uint16_t* part_o,
-                              const float* part_lse, uint16_t* o, float* lse, hipStream_t st);
+                              const float* part_lse, uint16_t* o, float* lse, const uint16_t* dout, float* Dd,
+                              hipStream_t st);
 
 hipError_t launch_bwd_dot(const Geo& g, const uint16_t* o, const uint16_t* dout, float* Dd, hipStream_t st);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);

@@ -134,4 +134,10 @@ hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const 
   return hipGetLastError();
 }
 
+hipError_t launch_inverse_items(const Geo& g, const InvBufs& ib, int item_tokens, hipStream_t st) {
+  k_inv_blockscan<<<g.B * g.G, 1024, 0, st>>>(ib.len, ib.base, ib.items, ib.item_count, g.N, ib.max_items,
+                                               item_tokens);
+  return hipGetLastError();
+}
+
 }  // namespace msa

@@ -86,7 +86,8 @@ typedef enum {
   MSA_OP_FWD = 1,
   MSA_OP_BWD = 2,
   MSA_OP_DECODE_SELECT = 3, /* msa_decode_select: B*G*(T/128) fp32 pooled scores */
-  MSA_OP_DECODE_FWD = 4     /* msa_decode_fwd: B*G*topk fp32 partials of R*(d+1) values */
+  MSA_OP_DECODE_FWD = 4,    /* msa_decode_fwd: B*G*topk fp32 partials of R*(d+1) values */
+  MSA_OP_FWD_BWD = 5        /* msa_fwd_bwd */
 } msa_op;
 
 /* Workspace that lets `op` process all tokens in one window (capped at a
@@ -150,6 +151,24 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
                    const msa_bf16* o, const msa_bf16* dout, const float* lse, const int32_t* idx,
                    msa_bf16* dq, msa_bf16* dk, msa_bf16* dv, void* ws, size_t ws_bytes,
                    void* stream);
+
+/* Merged forward and backward (keelcrux "Flash-MSA: Train on a million tokens
+ * without breaking the compute bank", section "The fact": forward and backward
+ * kernels are merged; section "Under the hood": activation memory cut about
+ * fivefold; the pages give no mechanism, this is the reading).  For a training
+ * step that runs a layer's backward right after its forward (the recompute
+ * pattern: between the two only q, k, v and the block-index cache are kept,
+ * not o and lse), one call writes o, lse exactly as msa_fwd and dq, dk, dv as
+ * msa_bwd given that o:
+ *   - each token window builds one inverse index that both halves use;
+ *   - D = rowsum(dout * o) of the bf16 o is formed by the forward combine
+ *     while o is in registers (no separate pass over o and dout);
+ *   - the dQ partials reuse the forward partials' workspace.
+ * Same layouts, shape rules and errors as msa_fwd / msa_bwd; dout is read,
+ * o and lse are written. */
+msa_status msa_fwd_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                       const msa_bf16* dout, const int32_t* idx, msa_bf16* o, float* lse, msa_bf16* dq, msa_bf16* dk,
+                       msa_bf16* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Decode step: one new query per sequence against its caches.
  * ai-beat "flash-msa-sparse-attention-training", paragraph 1: MSA also serves

@@ -197,7 +197,7 @@ def test_decode_checks(lib, msa):
     assert need_s >= 2 * 2 * 8 * 4                      # B*G*N fp32 pooled scores
     assert need_f >= 2 * 2 * 8 * 4 * (128 + 1) * 4      # B*G*topk partials of R*(d+1) fp32
     assert lib.msa_workspace_min_bytes(ctypes.byref(d), msa.OP_DECODE_FWD) == need_f
-    assert lib.msa_workspace_bytes(ctypes.byref(d), 5) == 0          # no such op
+    assert lib.msa_workspace_bytes(ctypes.byref(d), 6) == 0          # no such op
     assert sel(None, P, P, P, P, P, need_s, None) == ERR_NULL
     for i in range(5):
         args = [P] * 5
@@ -220,3 +220,26 @@ def test_decode_checks(lib, msa):
     for kw, code in ((dict(H=6, G=2), ERR_UNSUP), (dict(d=96), ERR_UNSUP), (dict(H=6, G=4), ERR_SHAPE)):
         bad = _dims(msa, **kw)
         assert fwd(ctypes.byref(bad), P, P, P, P, P, P, P, P, 1 << 40, None) == code, kw
+
+
+def test_fwd_bwd_checks(lib, msa):
+    P, Q = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    d = _dims(msa)
+    f = lib.msa_fwd_bwd
+    full = lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_FWD_BWD)
+    lo = lib.msa_workspace_min_bytes(ctypes.byref(d), msa.OP_FWD_BWD)
+    assert 0 < lo <= full
+    # one shared inverse index and aliased partials: below the two separate workspaces together
+    assert full < (lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_FWD) +
+                   lib.msa_workspace_bytes(ctypes.byref(d), msa.OP_BWD))
+    assert f(None, *([P] * 11), full, None) == ERR_NULL
+    for i in range(11):
+        args = [P] * 11
+        args[i] = None
+        assert f(ctypes.byref(d), *args, full, None) == ERR_NULL, i
+        args[i] = Q
+        assert f(ctypes.byref(d), *args, full, None) == ERR_ALIGN, i
+    assert f(ctypes.byref(d), *([P] * 11), lo - 1, None) == ERR_WS
+    for kw, code in ((dict(H=6, G=2), ERR_UNSUP), (dict(T=1000), ERR_SHAPE), (dict(d=96), ERR_UNSUP)):
+        bad = _dims(msa, **kw)
+        assert f(ctypes.byref(bad), *([P] * 11), 1 << 40, None) == code, kw
