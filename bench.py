@@ -43,28 +43,34 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "MSA fwd+bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), 128K & 1M"
 
 # Library timing slot -> kernel symbol prefix and the source file it is built from.
-KERNELS = {
-    "proxy_pool": ("k_proxy_pool<", "msa_select.hip"),
-    "topk": ("k_topk<", "msa_select.hip"),
-    "inverse": ("k_inv_scatter", "msa_inverse.hip"),
-    "fwd_partials": ("k_fwd_kv<", "msa_fwd.hip"),
-    "fwd_combine": ("k_fwd_combine<", "msa_fwd.hip"),
-    "bwd_dot": ("k_bwd_dot<", "msa_bwd.hip"),
-    "bwd_partials": ("k_bwd_kv<", "msa_bwd.hip"),
-    "dq_combine": ("k_dq_combine<", "msa_bwd.hip"),
-    "convert": ("k_cvt_bf16", "msa_bwd.hip"),
+KERNELS = {  # bench name -> (kernel symbol in rocprofv3 output, source files it is compiled from)
+    "proxy_pool": ("msa::k_proxy_pool<", ("msa_select.hip",)),
+    "topk": ("msa::k_topk<", ("msa_select.hip", "msa_topk.h")),
+    "inverse": ("msa::k_inv_scatter", ("msa_inverse.hip",)),
+    "fwd_partials": ("msa::k_fwd_kv<", ("msa_fwd.hip",)),
+    "fwd_combine": ("msa::k_fwd_combine<", ("msa_fwd.hip",)),
+    "bwd_dot": ("msa::k_bwd_dot<", ("msa_bwd.hip",)),
+    "bwd_partials": ("msa::k_bwd_kv<", ("msa_bwd.hip",)),
+    "dq_combine": ("msa::k_dq_combine<", ("msa_bwd.hip",)),
+    "convert": ("msa::k_cvt_bf16", ("msa_bwd.hip",)),
+    "dec_pool": ("msa::k_dec_pool<", ("msa_decode.hip",)),
+    "dec_topk": ("msa::k_dec_topk<", ("msa_decode.hip", "msa_topk.h")),
+    "dec_attn": ("msa::k_dec_attn<", ("msa_decode.hip",)),
+    "dec_combine": ("msa::k_dec_combine<", ("msa_decode.hip",)),
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msa_hbm_traffic_128k.md")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "msa_hbm_traffic_*.md")
 
 
 def kernel_source_hash(name: str) -> str:
-    """Hash of what a kernel is compiled from (its source, the shared headers and
+    """Hash of what a kernel is compiled from (its sources, the shared headers and
     the build flags): stored HBM counter figures apply only while it matches."""
     import hashlib
     csrc = os.path.join(ROOT, "block_sparse_attention_qk_amd", "csrc")
     h = hashlib.sha256()
-    for path in (os.path.join(csrc, KERNELS[name][1]), os.path.join(csrc, "msa_common.h"),
-                 os.path.join(csrc, "msa_internal.h"), os.path.join(ROOT, "block_sparse_attention_qk_amd", "build.py")):
+    paths = [os.path.join(csrc, f) for f in KERNELS[name][1]]
+    paths += [os.path.join(csrc, "msa_common.h"), os.path.join(csrc, "msa_internal.h"),
+              os.path.join(ROOT, "block_sparse_attention_qk_amd", "build.py")]
+    for path in paths:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -72,15 +78,15 @@ def kernel_source_hash(name: str) -> str:
 
 def stored_traffic(workload: str, name: str):
     """Calibrated HBM bytes per launch (read + write) of one kernel, from the
-    committed counter summary, or None if absent or taken on other code."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    for line in open(TRAFFIC_FILE):
-        f = dict(kv.split("=", 1) for kv in line.split()[1:] if "=" in kv) if line.startswith("traffic ") else {}
-        if f.get("workload") == workload and f.get("kernel") == name:
-            if f.get("source") != kernel_source_hash(name):
-                return None
-            return int(f["read_bytes"]) + int(f["write_bytes"])
+    committed counter summaries, or None if absent or taken on other code."""
+    import glob
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        for line in open(path):
+            f = dict(kv.split("=", 1) for kv in line.split()[1:] if "=" in kv) if line.startswith("traffic ") else {}
+            if f.get("workload") == workload and f.get("kernel") == name:
+                if f.get("source") != kernel_source_hash(name):
+                    return None
+                return int(f["read_bytes"]) + int(f["write_bytes"])
     return None
 
 
@@ -119,7 +125,7 @@ def pmc_summary(pmc_dir: str, copy_mib: int, workload: str) -> str:
         r_avg, w_avg = sum(rd) / len(rd), sum(wr) / len(wr)
         rb, wb = r_avg * factor["FETCH_SIZE"], w_avg * factor["WRITE_SIZE"]
         out.append("| %s (%s) | %d | %.0f | %.0f | %.3f | %.3f |" % (
-            name, sym.rstrip("<"), len(rd), r_avg / 1024, w_avg / 1024, rb / 2**30, wb / 2**30))
+            name, sym.split("::")[-1].rstrip("<"), len(rd), r_avg / 1024, w_avg / 1024, rb / 2**30, wb / 2**30))
         lines.append("traffic workload=%s kernel=%s read_bytes=%d write_bytes=%d source=%s" % (
             workload, name, rb, wb, kernel_source_hash(name)))
     return "\n".join(out + ["", "```"] + lines + ["```"])
@@ -315,8 +321,8 @@ def run_decode(cfg: synth.Config, B: int, steps: int, warmup: int) -> dict:
         ms, n = kern[name]
         avg_s = ms / n / 1e3
         rl[name] = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": work / avg_s / 1e9 / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": avg_s * 1e3,
-                    "work_per_launch": work}
+                    "frac": work / avg_s / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode-" + cfg.name, name),
+                    "avg_launch_ms": avg_s * 1e3, "work_per_launch": work}
     res = {
         "workload": "%s decode: B=%d sequences at %d cached tokens" % (cfg.name, B, cfg.T),
         "shape": {"B": B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk},
@@ -421,7 +427,8 @@ def main() -> int:
                          "(needs --copy-calibration-mib of those runs) and exit; no GPU needed")
     args = ap.parse_args()
     if args.pmc_summary:
-        print(pmc_summary(args.pmc_summary, args.copy_calibration_mib or 1024, args.config))
+        workload = "decode-" + args.decode_only if args.decode_only else args.config
+        print(pmc_summary(args.pmc_summary, args.copy_calibration_mib or 1024, workload))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
