@@ -13,10 +13,6 @@ namespace msa {
 namespace {
 
 constexpr size_t ALIGN = 256;
-// Backward items hold at most this many pairs: a block picked by more tokens
-// (early blocks, or a fixed pattern's far blocks that every query reads) is cut
-// into several items that run in parallel and add their dK/dV atomically.
-constexpr int BWD_ITEM_TOKENS = 4096;
 constexpr size_t CAP_SELECT = (size_t)8 << 30;
 constexpr size_t CAP_MAIN = (size_t)40 << 30;
 

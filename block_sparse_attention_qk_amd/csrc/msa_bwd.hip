@@ -67,6 +67,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) float rdd[3][TR];
   __shared__ __attribute__((aligned(16))) int rlim[3][TR];
   __shared__ __attribute__((aligned(16))) int rpair[3][TR];
+  __shared__ int lsts[BWD_ITEM_TOKENS];  // the item's pair list
 
   // Groups interleave in dispatch order (bg fastest) so that each group's
   // long early-block items start near the beginning of the launch.
@@ -100,7 +101,12 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       const int c = tid + BWD_THREADS * u, r = c / DCH, cc = c % DCH;
       st16u(&Ks[r * D + 8 * swz<DCH>(r, cc)], kr[u]);
     }
+    // The pair list goes to LDS, so that the producer's only global loads in
+    // its loop are the staged rows (a list lookup would otherwise wait for the
+    // staging loads issued before it).
+    for (int i = tid; i < len; i += BWD_THREADS) lsts[i] = lst[i];
   }
+  __syncthreads();
 
   if (wave < 4) {
     // =================== producer ===================
@@ -116,60 +122,69 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       }
     }
     // Staging: producer thread tid owns tile row tid/8 and chunks (tid%8) + 8u.
-    // Loads never branch and never wait where they are issued: a row past the
-    // list reads the list's last entry (finite data, masked at store time),
-    // the list entry of tile i+3 is fetched at the top of iteration i, and
-    // scaling and validity are applied when the staged registers go to LDS.
+    // A tile's rows are loaded two iterations before they go to LDS, into one
+    // of two register sets (tile parity), so each load has two tile times to
+    // arrive.  Loads never branch and never wait where they are issued: a row
+    // past the list reads the list's last entry (finite data, masked at store
+    // time), list entries come from LDS, and scaling and validity are applied
+    // when the staged registers go to LDS.
     const int srow = tid >> 3, ssub = tid & 7;
-    uint4 sq[CPT], sdo[CPT];
-    int s_li = len, s_pair = 0;
-    float s_lse = 0.f, s_dd = 0.f;
-    auto list_entry = [&](int ti) { return lst[min(ti * TT + srow / R, len - 1)]; };
-    auto stage_load = [&](int ti, int pair) {
-      s_li = ti * TT + srow / R;
-      s_pair = pair;
+    uint4 sq[2][CPT], sdo[2][CPT];
+    int s_li[2] = {len, len}, s_pair[2] = {0, 0};
+    float s_lse[2] = {0.f, 0.f}, s_dd[2] = {0.f, 0.f};
+    auto list_entry = [&](int ti) { return lsts[min(ti * TT + srow / R, len - 1)]; };
+    auto stage_load = [&](auto setc, int ti, int pair) {
+      constexpr int st = decltype(setc)::value;
+      s_li[st] = ti * TT + srow / R;
+      s_pair[st] = pair;
       const int t = t0 + pair / K;
       const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        sq[u] = ld16u(q + hrow * D + 8 * (ssub + 8 * u));
-        sdo[u] = ld16u(dout + hrow * D + 8 * (ssub + 8 * u));
+        sq[st][u] = ld16u(q + hrow * D + 8 * (ssub + 8 * u));
+        sdo[st][u] = ld16u(dout + hrow * D + 8 * (ssub + 8 * u));
       }
-      s_lse = lse[hrow];
-      s_dd = Dd[hrow];
+      s_lse[st] = lse[hrow];
+      s_dd[st] = Dd[hrow];
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](auto setc, int buf) {
+      constexpr int st = decltype(setc)::value;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int off = srow * D + 8 * swz<DCH>(srow, ssub + 8 * u);
-        st16u(&Qs[buf][off], sq[u]);
-        st16u(&dOs[buf][off], sdo[u]);
+        st16u(&Qs[buf][off], sq[st][u]);
+        st16u(&dOs[buf][off], sdo[st][u]);
       }
-      if (ssub == 0) {
-        const bool val = s_li < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
-        rlse[buf][srow] = val ? s_lse * LOG2E : INFINITY;
-        rdd[buf][srow] = s_dd * scale;
-        rlim[buf][srow] = val ? t0 + s_pair / K - blk * BLK : -1;
-        rpair[buf][srow] = val ? s_pair : -1;
-      }
+      // The row's 8 threads hold the same values and all write them: no branch,
+      // so the waits for the staging loads stay exact.
+      const bool val = s_li[st] < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
+      rlse[buf][srow] = val ? s_lse[st] * LOG2E : INFINITY;
+      rdd[buf][srow] = s_dd[st] * scale;
+      rlim[buf][srow] = val ? t0 + s_pair[st] / K - blk * BLK : -1;
+      rpair[buf][srow] = val ? s_pair[st] : -1;
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
 
-    stage_load(0, list_entry(0));
-    stage_store(0);
+    stage_load(I0{}, 0, list_entry(0));
+    stage_store(I0{}, 0);
     // All prologue loads (K and V operands included) complete here, so that the
     // loop's waits count only its own traffic.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bk[ks]), "+v"(bv[ks]));
-    stage_load(1, list_entry(1));
+    stage_load(I1{}, 1, list_entry(1));
+    stage_load(I0{}, 2, list_entry(2));
     __syncthreads();
 
-    // One iteration: compute tile i+1, stage tile i+2, load tile i+3.  The
-    // buffer indices are compile-time constants in each copy of the 6-way
-    // unrolled loop ((i+1) mod 3, (i+1) mod 2 and (i+2) mod 3).
-    auto produce = [&](auto qbc, auto pbc, auto sbc, int i) {
+    // One iteration: compute tile i+1, stage tile i+2, load tile i+4.  The
+    // buffer and register-set indices are compile-time constants in each copy
+    // of the 6-way unrolled loop ((i+1) mod 3, (i+1) mod 2, (i+2) mod 3 and
+    // i mod 2, the set that tile i+2 arrived in and tile i+4 loads into).
+    auto produce = [&](auto qbc, auto pbc, auto sbc, auto setc, int i) {
       constexpr int qb = decltype(qbc)::value, pb = decltype(pbc)::value, sb = decltype(sbc)::value;
-      const int pair3 = list_entry(i + 3);  // consumed by this iteration's staging load
+      const int pair4 = list_entry(i + 4);  // for this iteration's staging load
       if (i + 1 < ntiles) {
         const bf16raw* Qc = Qs[qb];
         const bf16raw* dOc = dOs[qb];
@@ -202,20 +217,21 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
           *reinterpret_cast<uint2*>(&dST[pb][o]) = make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3]));
         }
       }
-      stage_store(sb);  // tile i+2 (rows past the list are masked)
-      stage_load(i + 3, pair3);
+      stage_store(setc, sb);  // tile i+2 (rows past the list are masked)
+      stage_load(setc, i + 4, pair4);
       __syncthreads();
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    for (int i0 = -1; i0 < ntiles; i0 += 6) {  // i0 = -1 (mod 6): i0 + u computes tile 6m + u
-      produce(I0{}, I0{}, I1{}, i0);
-      if (i0 + 1 < ntiles) produce(I1{}, I1{}, I2{}, i0 + 1);
-      if (i0 + 2 < ntiles) produce(I2{}, I0{}, I0{}, i0 + 2);
-      if (i0 + 3 < ntiles) produce(I0{}, I1{}, I1{}, i0 + 3);
-      if (i0 + 4 < ntiles) produce(I1{}, I0{}, I2{}, i0 + 4);
-      if (i0 + 5 < ntiles) produce(I2{}, I1{}, I0{}, i0 + 5);
+    // i0 = -1 (mod 6): i0 + u computes tile 6m + u; the register set is (i0 + u) mod 2 = (u + 1) mod 2.
+    // The six steps run unconditionally (steps past the last tile only stage
+    // clamped rows), so the loop body is straight-line code and the waits for
+    // the staging loads count exactly; the consumer runs the same steps.
+    for (int i0 = -1; i0 < ntiles; i0 += 6) {
+      produce(I0{}, I0{}, I1{}, I1{}, i0);
+      produce(I1{}, I1{}, I2{}, I0{}, i0 + 1);
+      produce(I2{}, I0{}, I0{}, I1{}, i0 + 2);
+      produce(I0{}, I1{}, I1{}, I0{}, i0 + 3);
+      produce(I1{}, I0{}, I2{}, I1{}, i0 + 4);
+      produce(I2{}, I1{}, I0{}, I0{}, i0 + 5);
     }
   } else {
     // =================== consumer ===================
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     // lane offset plus an immediate.
     auto consume = [&](auto qbc, auto pbc, int i) {
       constexpr int qb = decltype(qbc)::value, pb = decltype(pbc)::value;
-      if (i >= 0) {
+      if (i >= 0 && i < ntiles) {
         const bf16raw* Qc = Qs[qb];
         const bf16raw* dOc = dOs[qb];
         // ---- dV += P^T dO, dK += dS^T Q : own keys x all head-dim tiles, the tile's 32 rows
@@ -251,17 +267,32 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
         }
         // ---- dQ^T tile = K^T dS^T : head-dim tile kq along M, the 32 rows along N, keys as K
         if (kq < NCT) {
+          // Both swizzles depend only on bits 0..3 of the row, which a step of 16
+          // keys leaves unchanged: k-step ks reads at a per-lane base plus a
+          // constant (16 rows of Ks, 16 rows of dS^T), and its operands are
+          // read two steps ahead of its MFMA.
+          const int kr0 = 8 * h + (i16 >> 2);
+          const int col = 32 * kq + 16 * g16 + 4 * (i16 & 3);
+          const int rc = 16 * g16 + 4 * (i16 & 3);
+          const bf16raw* ka0 = &Ks[kr0 * D + 8 * swz<DCH>(kr0, col >> 3) + (col & 7)];
+          const bf16raw* ka1 = &Ks[(kr0 + 4) * D + 8 * swz<DCH>(kr0 + 4, col >> 3) + (col & 7)];
+          const bf16raw* db0 = &dST[pb][kr0 * TR + 8 * pswz(kr0, rc >> 3) + (rc & 7)];
+          const bf16raw* db1 = &dST[pb][(kr0 + 4) * TR + 8 * pswz(kr0 + 4, rc >> 3) + (rc & 7)];
+          uint2 qa0[8], qa1[8], qb0[8], qb1[8];
+          auto rd = [&](int ks) {
+            qa0[ks] = lds_tr4(ka0 + 16 * ks * D);
+            qa1[ks] = lds_tr4(ka1 + 16 * ks * D);
+            qb0[ks] = lds_tr4(db0 + 16 * ks * TR);
+            qb1[ks] = lds_tr4(db1 + 16 * ks * TR);
+          };
+          rd(0);
+          rd(1);
           f32x16 dq = zero16();
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
-            const int kr = 16 * ks + 8 * h + (i16 >> 2);
-            const int col = 32 * kq + 16 * g16 + 4 * (i16 & 3);
-            const uint2 a0 = lds_tr4(&Ks[kr * D + 8 * swz<DCH>(kr, col >> 3) + (col & 7)]);
-            const uint2 a1 = lds_tr4(&Ks[(kr + 4) * D + 8 * swz<DCH>(kr + 4, col >> 3) + (col & 7)]);
-            const int rc = 16 * g16 + 4 * (i16 & 3);
-            const uint2 b0 = lds_tr4(&dST[pb][kr * TR + 8 * pswz(kr, rc >> 3) + (rc & 7)]);
-            const uint2 b1 = lds_tr4(&dST[pb][(kr + 4) * TR + 8 * pswz(kr + 4, rc >> 3) + (rc & 7)]);
-            dq = mfma32(as_bf8(make_uint4(a0.x, a0.y, a1.x, a1.y)), as_bf8(make_uint4(b0.x, b0.y, b1.x, b1.y)), dq);
+            if (ks + 2 < 8) rd(ks + 2);
+            dq = mfma32(as_bf8(make_uint4(qa0[ks].x, qa0[ks].y, qa1[ks].x, qa1[ks].y)),
+                        as_bf8(make_uint4(qb0[ks].x, qb0[ks].y, qb1[ks].x, qb1[ks].y)), dq);
           }
           // lane holds row l32, head-dim columns 32kq + 8j + 4h + (0..3); one lane
           // swap per dword gives lane half h whole 16-byte runs (columns 16pp + 8h .. +7)
@@ -290,11 +321,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     using I2 = std::integral_constant<int, 2>;
     for (int i0 = -1; i0 < ntiles; i0 += 6) {  // i0 = -1 (mod 6): i0 + u has i mod 3 = (u+2)%3, i mod 2 = (u+1)%2
       consume(I2{}, I1{}, i0);
-      if (i0 + 1 < ntiles) consume(I0{}, I0{}, i0 + 1);
-      if (i0 + 2 < ntiles) consume(I1{}, I1{}, i0 + 2);
-      if (i0 + 3 < ntiles) consume(I2{}, I0{}, i0 + 3);
-      if (i0 + 4 < ntiles) consume(I0{}, I1{}, i0 + 4);
-      if (i0 + 5 < ntiles) consume(I1{}, I0{}, i0 + 5);
+      consume(I0{}, I0{}, i0 + 1);
+      consume(I1{}, I1{}, i0 + 2);
+      consume(I2{}, I0{}, i0 + 3);
+      consume(I0{}, I1{}, i0 + 4);
+      consume(I1{}, I0{}, i0 + 5);
     }
 
     // ---- dK, dV of the owned keys: lane holds head-dim column 32c + l32, keys 32kq + 8j + 4h + i.

@@ -19,6 +19,10 @@ struct Win {
 
 constexpr int INV_CHUNK = 256;  // tokens per counting-sort chunk
 constexpr int FWD_ITEM_TOKENS = 256;  // tokens per forward work item (list chunk)
+// Backward items hold at most this many pairs: a block picked by more tokens
+// (early blocks, or a fixed pattern's far blocks that every query reads) is cut
+// into several items that run in parallel and add their dK/dV atomically.
+constexpr int BWD_ITEM_TOKENS = 4096;
 
 // ---- Index Branch
 hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,
