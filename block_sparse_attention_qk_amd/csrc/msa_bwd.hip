@@ -307,10 +307,10 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
             run[pp] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
           }
           const int p = rpair[qb][l32];  // the same for both lane halves of a row
-          if (p >= 0) {
-            bf16raw* dst = dq_part + ((pair0 + (size_t)p) * R + l32 % R) * D + 32 * kq + 8 * h;
-            st16u(dst, run[0]);
-            st16u(dst + 16, run[1]);
+          if (p >= 0) {  // runs 2k + h of head l32 % R, k = 2kq + pp, in the slot's run-interleaved layout
+            bf16raw* dst = dq_part + (pair0 + (size_t)p) * R * D + 16 * (l32 % R) + 8 * h;
+            st16u(dst + 16 * R * (2 * kq), run[0]);
+            st16u(dst + 16 * R * (2 * kq + 1), run[1]);
           }
         }
       }
@@ -397,11 +397,11 @@ __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ 
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int bg = row / W, tl = row % W, t = t0 + tl, b = bg / G, g = bg % G;
-  const int hh = sub / (D / 8), c8 = (sub % (D / 8)) * 8;
+  const int hh = sub / (D / 8), run = sub % (D / 8), c8 = run * 8;
   const int32_t* ir = idx + ((size_t)bg * T + t) * K;
   const size_t p0 = (size_t)bg * W * K + (size_t)tl * K;
   const unsigned last = (unsigned)(t / BLK);
-  const bf16raw* pp = part + (p0 * R + hh) * D + c8;
+  const bf16raw* pp = part + p0 * R * D + partial_run_offset<R>(hh, run);
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;

@@ -114,6 +114,17 @@ __device__ __forceinline__ void st4bf(void* p, float a, float b, float c, float 
   *reinterpret_cast<uint2*>(p) = make_uint2(pack2(a, b), pack2(c, d));
 }
 
+// Per-pair partial slots (forward o_b and backward dQ partials) hold R rows
+// of D bf16 as 16-byte runs (run j = columns 8j .. 8j+7) in the order
+// [j / 2][head][j % 2]: the two lanes that hold a row after an MFMA write
+// runs 2k and 2k+1, so one 16-byte store instruction covers 32 contiguous
+// bytes of each of R heads, i.e. 32 R contiguous bytes per pair.  Element
+// offset of run j of head hh within a slot:
+template <int R>
+__device__ __forceinline__ int partial_run_offset(int hh, int j) {
+  return (j >> 1) * 16 * R + 16 * hh + 8 * (j & 1);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

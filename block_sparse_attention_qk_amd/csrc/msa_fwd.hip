@@ -184,8 +184,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
       const size_t pidx = cpr >= 0 ? pair0 + (size_t)cpr : (size_t)BG * W * K;
       // Lane halves h = 0/1 hold head-dim columns 8j + 0..3 / 8j + 4..7 of the
       // same row; one lane swap per dword gives lane h whole 16-byte runs
-      // (columns 16p + 8h .. +7 of each 32-column tile), stored as one 16-byte write.
-      bf16raw* dst = part_o + (pidx * R + hh) * D + 8 * h;
+      // (run 2k + h, k = 2ct + pp, = columns 16k + 8h .. +7), stored as one
+      // 16-byte write into the pair's slot in the run-interleaved layout, where
+      // one store instruction fills 256 contiguous bytes of each of its pairs.
+      bf16raw* dst = part_o + pidx * R * D + 16 * hh + 8 * h;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
           const uint32_t w1 = pack2(oacc[ct][e1 + 2] * inv, oacc[ct][e1 + 3] * inv);
           const auto s0 = __builtin_amdgcn_permlane32_swap(u0, w0, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(u1, w1, false, false);
-          st16u(dst + 32 * ct + 16 * pp, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+          st16u(dst + 16 * R * (2 * ct + pp), make_uint4(s0[0], s1[0], s0[1], s1[1]));
         }
       part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;  // both lane halves hold the same value
     }
@@ -222,12 +224,12 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int bg = row / W, tl = row % W, t = t0 + tl, b = bg / G, g = bg % G;
-  const int hh = sub / (D / 8), c8 = (sub % (D / 8)) * 8;
+  const int hh = sub / (D / 8), run = sub % (D / 8), c8 = run * 8;
   const int32_t* ir = idx + ((size_t)bg * T + t) * K;
   const size_t p0 = (size_t)bg * W * K + (size_t)tl * K;
   const unsigned last = (unsigned)(t / BLK);
   const float* pl = part_lse + p0 * R + hh;
-  const bf16raw* po = part_o + (p0 * R + hh) * D + c8;
+  const bf16raw* po = part_o + p0 * R * D + partial_run_offset<R>(hh, run);
   const size_t orow = (size_t)(b * T + t) * H + g * R + hh;
   uint4 dch = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (WITH_D) dch = ld16u(dout + orow * D + c8);  // issued ahead of the slot stream
