@@ -41,14 +41,37 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
   int need = nsel;  // rank of the wanted key among keys matching prefix
   if constexpr (VPL <= 16) {
     // Short rows: build the k-th largest key bit by bit from the top; each
-    // step is one ballot count per register of keys.
-    for (int bit = 31; bit >= 0; --bit) {
+    // step is one ballot count per register of keys.  The bits that the row's
+    // smallest and largest keys share are taken as they are (every key has
+    // them), and the search stops once exactly nsel keys lie at or above the
+    // prefix: the lower bits could then no longer change which keys are
+    // chosen, and no unchosen key equals a chosen one.
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i * 64 + lane < nc) {
+        kmin = min(kmin, key[i]);
+        kmax = max(kmax, key[i]);
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    const uint32_t diff = kmin ^ kmax;
+    int bit = diff == 0u ? -1 : 31 - __builtin_clz(diff);  // highest bit not shared by all keys
+    prefix = bit < 0 ? kmax : (bit == 31 ? 0u : kmax & ~((2u << bit) - 1u));
+    int cge = nc;  // keys at or above prefix
+    for (; bit >= 0 && cge != nsel; --bit) {
       const uint32_t cand = prefix | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
         if (i * 64 < nc) cnt += __popcll(__ballot((i * 64 + lane < nc) && key[i] >= cand));
-      if (cnt >= nsel) prefix = cand;
+      if (cnt >= nsel) {
+        prefix = cand;
+        cge = cnt;
+      }
     }
     int cnt_gt = 0;
 #pragma unroll
