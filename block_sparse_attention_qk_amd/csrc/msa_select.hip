@@ -114,21 +114,32 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
     const bool need_mask = kb * BLK + BLK - 1 > qt0 + 32 * wave;  // keys past some query of this wave
     const int lim = tq - kb * BLK;
     float mx = -INFINITY;
+    // The causal mask is a separate compile-time path: blocks that no query of
+    // the wave crosses (all but the last one or two) take only the maxima.
+    auto tiles = [&](auto maskc) {
+      constexpr bool MASK = decltype(maskc)::value;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {  // 32-key tiles (other waves of the SIMD cover the MFMA chain)
-      f32x16 acc = zero16();
-      const int r = 32 * mt + l32;
+      for (int mt = 0; mt < 4; ++mt) {  // 32-key tiles (other waves of the SIMD cover the MFMA chain)
+        f32x16 acc = zero16();
+        const int r = 32 * mt + l32;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(&kc[r * DP + 8 * kswz<DP>(r, 2 * ks + h)]), bq[ks], acc);
-      // lane holds query column l32 and keys 32mt + 8(e/4) + 4h + e%4
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(&kc[r * DP + 8 * kswz<DP>(r, 2 * ks + h)]), bq[ks], acc);
+        // lane holds query column l32 and keys 32mt + 8(e/4) + 4h + e%4
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float sv = acc[e];
-        if (need_mask && 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3) > lim) sv = -INFINITY;
-        mx = fmaxf(mx, sv);
+        for (int e = 0; e < 16; ++e) {
+          float sv = acc[e];
+          if constexpr (MASK) {
+            if (32 * mt + 8 * (e >> 2) + 4 * h + (e & 3) > lim) sv = -INFINITY;
+          }
+          mx = fmaxf(mx, sv);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep later tiles' operand reads from piling up in registers
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep later tiles' operand reads from piling up in registers
-    }
+    };
+    if (need_mask)
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
     {
       float m = fmaxf(mx, __shfl_xor(mx, 32));
       if (m == 0.0f) m = 0.0f;  // -0 and +0 rank equal
