@@ -1,6 +1,8 @@
 // Per-row top-k of pooled block scores, one row per wavefront, shared by the
 // training-shape and decode-shape Index Branch kernels.
 #pragma once
+#include <climits>
+
 #include "msa_common.h"
 
 namespace msa {
@@ -38,7 +40,8 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
   }
 
   uint32_t prefix = 0;
-  int need = nsel;  // rank of the wanted key among keys matching prefix
+  int need = nsel;      // rank of the wanted key among keys matching prefix
+  bool all_eq = false;  // every key equal to the final prefix is taken
   if constexpr (VPL <= 16) {
     // Short rows: build the k-th largest key bit by bit from the top; each
     // step is one ballot count per register of keys.  The bits that the row's
@@ -131,19 +134,30 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
     uint32_t run = __shfl(excl, owner);
     const int otop = nbins - per * owner;
     int bin = otop - 1;
+    uint32_t cbin = 0;  // keys in the chosen bin
     for (int j = 0; j < per; ++j) {  // every lane walks the owner's bins (LDS broadcast)
       const uint32_t c = hist[otop - 1 - j];
-      if (run + c >= (uint32_t)need) { bin = otop - 1 - j; break; }
+      if (run + c >= (uint32_t)need) {
+        bin = otop - 1 - j;
+        cbin = c;
+        break;
+      }
       run += c;
     }
     need -= (int)run;
     prefix |= (uint32_t)bin << sh;
     bits = sh;
+    // The chosen bin holds exactly the keys still needed: all of them are taken,
+    // the lower digits cannot change that, and no other key ties with them.
+    if (cbin == (uint32_t)need) {
+      all_eq = true;
+      break;
+    }
     __builtin_amdgcn_wave_barrier();
   }
   }
   const uint32_t kth = prefix;
-  const int need_eq = need;  // equal keys to take, lowest block index first
+  const int need_eq = all_eq ? INT_MAX : need;  // equal keys to take, lowest block index first
 
   const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int run_eq = 0, run_sel = 0;

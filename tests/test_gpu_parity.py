@@ -253,3 +253,23 @@ def test_512k_config_gpu_generated(msa, oracle_mod):
 
 def test_1m_config_gpu_generated(msa, oracle_mod):
     _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=128, blocks_from_end=[0, 1])
+
+
+@pytest.mark.parametrize("T,topk", [(1 << 18, 40), (1 << 20, 288)])
+def test_long_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
+    """Rows longer than 1024 blocks go through the radix select.  A proxy-key
+    cache that repeats one 128-row block gives every complete block the same
+    pooled score, so the lowest block ids must win (and match the oracle)."""
+    print("long-row ties", T, topk, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(17)
+    base = torch.randn((128, G, dp), generator=g).to(torch.bfloat16)
+    kp = base.repeat(T // 128, 1, 1).unsqueeze(0).contiguous()
+    qp = torch.randn((1, T, G, dp), generator=g).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([T - 1, T - 200, T // 2 + 77, 300 * 128 + 5, 200 * 128 + 127])
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
