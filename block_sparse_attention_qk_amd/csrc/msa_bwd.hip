@@ -69,10 +69,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) int rpair[3][TR];
   __shared__ int lsts[BWD_ITEM_TOKENS];  // the item's pair list
 
-  // Groups interleave in dispatch order (bg fastest) so that each group's
-  // long early-block items start near the beginning of the launch.
-  const int BG = (int)gridDim.x / max_items;
-  const int bg = (int)blockIdx.x % BG, item = (int)blockIdx.x / BG;
+  // Groups run one after another in dispatch order: the query rows that the
+  // running items re-read are one group's, which the last-level cache holds
+  // better than all groups' (items are capped at BWD_ITEM_TOKENS pairs, so no
+  // single item dominates the tail).
+  const int bg = (int)blockIdx.x / max_items, item = (int)blockIdx.x % max_items;
   if (item >= item_count[bg]) return;
   const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
@@ -309,8 +310,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
           const int p = rpair[qb][l32];  // the same for both lane halves of a row
           if (p >= 0) {  // runs 2k + h of head l32 % R, k = 2kq + pp, in the slot's run-interleaved layout
             bf16raw* dst = dq_part + (pair0 + (size_t)p) * R * D + 16 * (l32 % R) + 8 * h;
-            st16u(dst + 16 * R * (2 * kq), run[0]);
-            st16u(dst + 16 * R * (2 * kq + 1), run[1]);
+            st16nt(dst + 16 * R * (2 * kq), run[0]);
+            st16nt(dst + 16 * R * (2 * kq + 1), run[1]);
           }
         }
       }

@@ -77,6 +77,14 @@ __device__ __forceinline__ void st8(void* p, const bf16x8& v) { *reinterpret_cas
 
 __device__ __forceinline__ uint4 ld16u(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16u(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// 16-byte store marked non-temporal: data written once and read back much
+// later (the per-pair partials) streams past the caches instead of evicting
+// rows that are still being re-read.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+__device__ __forceinline__ void st16nt(void* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ bf16x8 as_bf8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Transposing two 8-element rows a, b (as 4 words each) into 8 words of

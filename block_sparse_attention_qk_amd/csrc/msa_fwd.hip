@@ -44,10 +44,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   __shared__ __attribute__((aligned(16))) bf16raw Vs[BLK * D];
   __shared__ int lsts[FWD_ITEM_TOKENS];  // the item's pair list (items hold at most FWD_ITEM_TOKENS pairs)
 
-  // Groups interleave in dispatch order (bg fastest) so that each group's
-  // long early-block items start near the beginning of the launch.
+  // Groups run one after another in dispatch order (items are short, so the
+  // order does not unbalance the launch): the Q rows the running items re-read
+  // are one group's, a quarter of Q at G = 4, which stays in the last-level cache.
   const int BG = (int)gridDim.x / max_items;
-  const int bg = (int)blockIdx.x % BG, item = (int)blockIdx.x / BG;
+  const int bg = (int)blockIdx.x / max_items, item = (int)blockIdx.x % max_items;
   if (item >= item_count[bg]) return;
   const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
           const uint32_t w1 = pack2(oacc[ct][e1 + 2] * inv, oacc[ct][e1 + 3] * inv);
           const auto s0 = __builtin_amdgcn_permlane32_swap(u0, w0, false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(u1, w1, false, false);
-          st16u(dst + 16 * R * (2 * ct + pp), make_uint4(s0[0], s1[0], s0[1], s1[1]));
+          st16nt(dst + 16 * R * (2 * ct + pp), make_uint4(s0[0], s1[0], s0[1], s1[1]));
         }
       part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;  // both lane halves hold the same value
     }
