@@ -13,6 +13,10 @@ namespace msa {
 namespace {
 
 constexpr size_t ALIGN = 256;
+// The forward walks token windows whose query rows of one group (W R d bf16)
+// stay within this many bytes: the items of a group re-read those rows once
+// per selected block, and the last-level cache then serves most re-reads.
+constexpr size_t FWD_WINDOW_Q_BYTES = (size_t)64 << 20;
 constexpr size_t CAP_SELECT = (size_t)8 << 30;
 constexpr size_t CAP_MAIN = (size_t)40 << 30;
 
@@ -107,6 +111,15 @@ int fit_window(const Geo& g, msa_op op, size_t bytes) {
   }
   if (lo == 0) return layout(g, op, min_window(g)).total <= bytes ? min_window(g) : 0;
   return 256 * lo;
+}
+
+// Largest forward window (T, or a multiple of 256 tokens) whose query rows of
+// one group fit FWD_WINDOW_Q_BYTES.
+int fwd_window_cap(const Geo& g) {
+  const size_t row = (size_t)g.R * g.D * 2;
+  const size_t w = FWD_WINDOW_Q_BYTES / row;
+  if (w >= (size_t)g.T) return g.T;
+  return std::max<int>(256, (int)(w / 256 * 256));
 }
 
 bool is_pow2_le16(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
@@ -209,7 +222,8 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
   if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
   if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_FWD_BWD) return 0;
   if (make_geo(dims, op, &g) != MSA_OK) return 0;
-  const size_t full = layout(g, op, g.T).total;
+  const int pref = (op == MSA_OP_FWD || op == MSA_OP_FWD_BWD) ? fwd_window_cap(g) : g.T;
+  const size_t full = layout(g, op, pref).total;
   const size_t cap = op == MSA_OP_SELECT ? CAP_SELECT : CAP_MAIN;
   if (full <= cap) return full;
   const int W = fit_window(g, op, cap);
@@ -275,8 +289,9 @@ msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   if (s != MSA_OK) return s;
   if (!q || !k || !v || !idx || !o || !lse || !ws) return MSA_ERR_NULL;
   if (!al16(q) || !al16(k) || !al16(v) || !al16(idx) || !al16(o) || !al16(lse) || !al16(ws)) return MSA_ERR_ALIGN;
-  const int W = fit_window(g, MSA_OP_FWD, ws_bytes);
+  int W = fit_window(g, MSA_OP_FWD, ws_bytes);
   if (W == 0) return MSA_ERR_WORKSPACE;
+  W = std::min(W, fwd_window_cap(g));
   const Layout L = layout(g, MSA_OP_FWD, W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
@@ -337,8 +352,9 @@ msa_status msa_fwd_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* 
   if (!al16(q) || !al16(k) || !al16(v) || !al16(dout) || !al16(idx) || !al16(o) || !al16(lse) || !al16(dq) ||
       !al16(dk) || !al16(dv) || !al16(ws))
     return MSA_ERR_ALIGN;
-  const int W = fit_window(g, MSA_OP_FWD_BWD, ws_bytes);
+  int W = fit_window(g, MSA_OP_FWD_BWD, ws_bytes);
   if (W == 0) return MSA_ERR_WORKSPACE;
+  W = std::min(W, fwd_window_cap(g));
   const Layout L = layout(g, MSA_OP_FWD_BWD, W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);

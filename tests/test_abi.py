@@ -149,10 +149,13 @@ def test_workspace_sizes(msa):
             lo = msa.msa_workspace_min_bytes(*shape, op)
             assert 0 < lo <= full, (name, op)
             assert full <= (40 << 30) + (16 << 30), (name, op, full)  # capped (plus T-sized accumulators)
-    # 128K runs the main branch in one window: the pair partials of all tokens fit.
+    # 128K runs the backward in one window (the pair partials of all tokens fit)
+    # and the forward in 32768-token windows (64 MiB of query rows per group).
     B, T, H, G, d, dp, k = 1, 131072, 32, 4, 128, 64, 32
     pairs_bytes = B * G * T * k * (H // G) * d * 2
-    assert msa.msa_workspace_bytes(B, T, H, G, d, dp, k, msa.OP_FWD) > pairs_bytes
+    assert msa.msa_workspace_bytes(B, T, H, G, d, dp, k, msa.OP_BWD) > pairs_bytes
+    fwd = msa.msa_workspace_bytes(B, T, H, G, d, dp, k, msa.OP_FWD)
+    assert pairs_bytes // 4 < fwd < pairs_bytes // 2
 
 
 def test_binding_rejects_host_tensors(msa):
