@@ -178,6 +178,184 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
   topk_row<VPL>(pooled + (size_t)row * N, t / BLK + 1, K, idx + ((size_t)bg * T + t) * K, hist_all[wave], lane);
 }
 
+// Long rows (more than 1024 blocks): one 512-thread workgroup per row, VPT
+// keys per thread in columns i*512 + tid.  A wave per row would need 64 key
+// registers or more per lane at these lengths (one wave per SIMD, spilled
+// scalars); here each thread holds at most 16 keys and eight waves share the
+// radix select: the same digits as the wave routine (11 bits below the row's
+// common prefix), histograms in LDS, a workgroup scan from the top bin, the
+// same early stop when the chosen bin holds exactly the keys still needed,
+// and the same tie rule (keys equal to the k-th taken lowest block first).
+constexpr int TKW_THREADS = 512;
+constexpr int TKW_WAVES = TKW_THREADS / 64;
+
+template <int VPT>
+__global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict__ pooled,
+                                                         int32_t* __restrict__ idx, int T, int N, int K, int t0,
+                                                         int W) {
+  constexpr int PER = TOPK_BINS / TKW_THREADS;  // bins per thread in the scan of an 11-bit digit
+  __shared__ uint32_t hist[TOPK_BINS];
+  __shared__ uint32_t red[2][TKW_WAVES];
+  __shared__ uint32_t wsum[TKW_WAVES];
+  __shared__ int bc[3];
+  __shared__ uint16_t ceq[VPT][TKW_WAVES], csel[VPT][TKW_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;  // the grid holds exactly the window's rows
+  const int bg = row / W, t = t0 + row % W;
+  const int nc = t / BLK + 1, nsel = min(K, nc);
+  const float* pr = pooled + (size_t)row * N;
+  int32_t* out = idx + ((size_t)bg * T + t) * K;
+
+  uint32_t key[VPT];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int col = i * TKW_THREADS + tid;
+    uint32_t kk = 0;
+    if (col < nc) {
+      float f = pr[col];
+      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
+      const uint32_t u = __float_as_uint(f);
+      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
+    }
+    key[i] = kk;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < TKW_WAVES; ++w) {
+    kmin = min(kmin, red[0][w]);
+    kmax = max(kmax, red[1][w]);
+  }
+  // Radix select of the nsel-th largest key below the common prefix of kmin and kmax.
+  const uint32_t diff = kmin ^ kmax;
+  int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);
+  uint32_t prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
+  int need = nsel;      // rank of the wanted key among the keys matching prefix
+  bool all_eq = false;  // every key equal to the final prefix is taken
+  while (bits > 0) {    // bits, prefix and need are the same in every thread
+    const int width = bits < 11 ? bits : 11;
+    const int sh = bits - width, nbins = 1 << width;
+    const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
+    for (int j = tid; j < nbins; j += TKW_THREADS) hist[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (i * TKW_THREADS + tid < nc && (key[i] & hi_mask) == prefix)
+        atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
+    __syncthreads();
+    // thread tid owns the bins [top - PER, top) counted from the top bin down
+    const int top = nbins - PER * tid;
+    uint32_t c[PER], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      c[j] = top - 1 - j >= 0 ? hist[top - 1 - j] : 0u;
+      lsum += c[j];
+    }
+    uint32_t incl = lsum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TKW_WAVES; ++w)
+      if (w < wave) incl += wsum[w];
+    const uint32_t excl = incl - lsum;
+    if (excl < (uint32_t)need && (uint32_t)need <= incl) {  // exactly one thread
+      uint32_t run = excl;
+      int bin = top - 1;
+      uint32_t cbin = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (run + c[j] >= (uint32_t)need) {
+          bin = top - 1 - j;
+          cbin = c[j];
+          break;
+        }
+        run += c[j];
+      }
+      bc[0] = bin;
+      bc[1] = need - (int)run;
+      bc[2] = (int)cbin;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << sh;
+    need = bc[1];
+    bits = sh;
+    // The chosen bin holds exactly the keys still needed: all of them are taken,
+    // the lower digits cannot change that, and no other key ties with them.
+    if (bc[2] == need) {
+      all_eq = true;
+      break;
+    }
+    // hist, wsum and bc are next written after two more barriers: no barrier here
+  }
+  const uint32_t kth = prefix;
+  const int need_eq = all_eq ? INT_MAX : need;  // equal keys to take, lowest block index first
+
+  // Ascending write-out over columns i*512 + tid: per (column group, wave)
+  // counts of equal keys, then of chosen keys, each followed by one barrier.
+  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const bool eq = i * TKW_THREADS + tid < nc && key[i] == kth;
+    const unsigned long long meq = __ballot(eq);
+    if (lane == 0) ceq[i][wave] = (uint16_t)__popcll(meq);
+  }
+  __syncthreads();
+  bool selv[VPT];
+  int eq_base = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const bool valid = i * TKW_THREADS + tid < nc;
+    const bool eq = valid && key[i] == kth, gt = valid && key[i] > kth;
+    int before = eq_base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < TKW_WAVES; ++w) {
+      const int cw = ceq[i][w];
+      before += w < wave ? cw : 0;
+      tot += cw;
+    }
+    const unsigned long long meq = __ballot(eq);
+    selv[i] = gt || (eq && before + __popcll(meq & lt) < need_eq);
+    const unsigned long long msel = __ballot(selv[i]);
+    if (lane == 0) csel[i][wave] = (uint16_t)__popcll(msel);
+    eq_base += tot;
+  }
+  __syncthreads();
+  int sel_base = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    int before = sel_base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < TKW_WAVES; ++w) {
+      const int cw = csel[i][w];
+      before += w < wave ? cw : 0;
+      tot += cw;
+    }
+    const unsigned long long msel = __ballot(selv[i]);
+    const int pos = before + __popcll(msel & lt);
+    if (selv[i] && pos < nsel) out[pos] = i * TKW_THREADS + tid;
+    sel_base += tot;
+  }
+  for (int p = nsel + tid; p < K; p += TKW_THREADS) out[p] = -1;
+}
+
 hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,
                              float* pooled, hipStream_t st) {
   dim3 grid((w.W + POOL_QT - 1) / POOL_QT, g.B * g.G), block(64 * POOL_WAVES);
@@ -204,10 +382,18 @@ hipError_t launch_topk(const Geo& g, const Win& w, const float* pooled, int32_t*
   MSA_TOPK_CASE(4)
   MSA_TOPK_CASE(8)
   MSA_TOPK_CASE(16)
-  MSA_TOPK_CASE(32)
-  MSA_TOPK_CASE(64)
-  MSA_TOPK_CASE(128)
 #undef MSA_TOPK_CASE
+  // rows of more than 1024 blocks: one workgroup per row
+  const int vpt = (g.N + TKW_THREADS - 1) / TKW_THREADS;
+#define MSA_TOPK_WG_CASE(V)                                                                 \
+  if (vpt <= V) {                                                                           \
+    k_topk_wg<V><<<dim3(rows), dim3(TKW_THREADS), 0, st>>>(pooled, idx, g.T, g.N, g.K, w.t0, w.W); \
+    return hipGetLastError();                                                               \
+  }
+  MSA_TOPK_WG_CASE(4)
+  MSA_TOPK_WG_CASE(8)
+  MSA_TOPK_WG_CASE(16)
+#undef MSA_TOPK_WG_CASE
   return hipErrorInvalidValue;
 }
 

@@ -273,3 +273,25 @@ def test_long_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
     got = idx[0, 0].cpu().numpy()[rows]
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
+@pytest.mark.parametrize("T,G,topk,n_rows", [(1 << 18, 2, 64, 1536), (1 << 20, 1, 288, 384)])
+def test_long_rows_many_rows_match_oracle(msa, oracle_mod, T, G, topk, n_rows):
+    """Rows longer than 1024 blocks are selected by one workgroup per row.
+    Proxy inputs follow the block-mean recipe; a seeded sample of rows over the
+    whole sequence (short rows, rows around 1024 blocks, the last rows) must
+    match the oracle bit-exactly up to near-ties."""
+    print("long rows", T, G, topk, flush=True)
+    cfg = synth.Config("long%d" % T, 1, T, G, G, 64, 32, topk)
+    qp = synth.make_tensor("qp", cfg, seed_offset=31)
+    kp = synth.make_tensor("kp", cfg, seed_offset=31)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([rng.choice(T, size=n_rows - 6, replace=False),
+                                     [0, 1023 * 128, 1024 * 128 + 5, T // 2, T - 2, T - 1]]))
+    dm = Dims(1, T, G, G, 64, 32, topk)
+    idx_ref, pooled = oracle_mod.select(dm, qp, kp, rows=rows, return_pooled=True)
+    got = idx[0].cpu().numpy()[:, rows, :].transpose(1, 0, 2)
+    info = parity.check_indices(got, idx_ref, pooled, topk)
+    print("indices", info, flush=True)
