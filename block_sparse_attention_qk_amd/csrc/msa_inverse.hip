@@ -12,37 +12,55 @@
 
 namespace msa {
 
+constexpr int INV_THREADS = 512;  // threads per counting-sort workgroup
+constexpr int INV_UNROLL = 8;     // cache entries each thread loads before its LDS atomics
+
 // counts[bg][chunk][blk] = number of pairs of the chunk's tokens that picked blk.
 // Entries outside 0..t/128 are ignored.
-__global__ __launch_bounds__(256) void k_inv_count(const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
-                                                   int T, int N, int K, int t0, int W, int nchunk) {
+__global__ __launch_bounds__(INV_THREADS) void k_inv_count(const int32_t* __restrict__ idx,
+                                                           int32_t* __restrict__ counts, int T, int N, int K,
+                                                           int t0, int W, int nchunk) {
   extern __shared__ int32_t hist[];
   const int chunk = blockIdx.x, bg = blockIdx.y;
-  for (int i = threadIdx.x; i < N; i += 256) hist[i] = 0;
+  for (int i = threadIdx.x; i < N; i += INV_THREADS) hist[i] = 0;
   __syncthreads();
-  const int tl0 = chunk * INV_CHUNK, ntok = min(INV_CHUNK, W - tl0);
+  const int tl0 = chunk * INV_CHUNK, n = min(INV_CHUNK, W - tl0) * K;
   const int32_t* rows = idx + ((size_t)bg * T + t0 + tl0) * K;
-  for (int e = threadIdx.x; e < ntok * K; e += 256) {
-    const int blk = rows[e];
-    const int t = t0 + tl0 + e / K;
-    if (blk >= 0 && blk <= t / BLK) atomicAdd(&hist[blk], 1);
+  for (int e0 = threadIdx.x; e0 < n; e0 += INV_THREADS * INV_UNROLL) {
+    int blk[INV_UNROLL];
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) {
+      const int e = e0 + u * INV_THREADS;
+      blk[u] = e < n ? rows[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) {
+      const int e = e0 + u * INV_THREADS;
+      if (blk[u] >= 0 && blk[u] <= (t0 + tl0 + e / K) / BLK) atomicAdd(&hist[blk[u]], 1);
+    }
   }
   __syncthreads();
   int32_t* out = counts + ((size_t)bg * nchunk + chunk) * N;
-  for (int i = threadIdx.x; i < N; i += 256) out[i] = hist[i];
+  for (int i = threadIdx.x; i < N; i += INV_THREADS) out[i] = hist[i];
 }
 
 // In place: counts[bg][c][blk] <- sum over chunks before c; len[bg][blk] = total.
+// Eight chunks' counts are loaded before their prefixes are stored.
 __global__ __launch_bounds__(256) void k_inv_colscan(int32_t* __restrict__ counts, int32_t* __restrict__ len,
                                                      int N, int nchunk) {
   const int bg = blockIdx.y, blk = blockIdx.x * 256 + threadIdx.x;
   if (blk >= N) return;
+  int32_t* col = counts + (size_t)bg * nchunk * N + blk;
   int run = 0;
-  for (int c = 0; c < nchunk; ++c) {
-    const size_t o = ((size_t)bg * nchunk + c) * N + blk;
-    const int v = counts[o];
-    counts[o] = run;
-    run += v;
+  for (int c0 = 0; c0 < nchunk; c0 += INV_UNROLL) {
+    int v[INV_UNROLL];
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) v[u] = c0 + u < nchunk ? col[(size_t)(c0 + u) * N] : 0;
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) {
+      if (c0 + u < nchunk) col[(size_t)(c0 + u) * N] = run;
+      run += v[u];
+    }
   }
   len[(size_t)bg * N + blk] = run;
 }
@@ -92,24 +110,34 @@ __global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restric
 }
 
 // list[bg][pos] = (t - t0) * K + slot, grouped by block.
-__global__ __launch_bounds__(256) void k_inv_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ base, int32_t* __restrict__ list,
-                                                     int T, int N, int K, int t0, int W, int nchunk) {
+__global__ __launch_bounds__(INV_THREADS) void k_inv_scatter(const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ list, int T, int N, int K, int t0,
+                                                             int W, int nchunk) {
   extern __shared__ int32_t cur[];
   const int chunk = blockIdx.x, bg = blockIdx.y;
   const int32_t* cc = counts + ((size_t)bg * nchunk + chunk) * N;
   const int32_t* bs = base + (size_t)bg * N;
-  for (int i = threadIdx.x; i < N; i += 256) cur[i] = bs[i] + cc[i];
+  for (int i = threadIdx.x; i < N; i += INV_THREADS) cur[i] = bs[i] + cc[i];
   __syncthreads();
-  const int tl0 = chunk * INV_CHUNK, ntok = min(INV_CHUNK, W - tl0);
+  const int tl0 = chunk * INV_CHUNK, n = min(INV_CHUNK, W - tl0) * K;
   const int32_t* rows = idx + ((size_t)bg * T + t0 + tl0) * K;
   int32_t* out = list + (size_t)bg * W * K;
-  for (int e = threadIdx.x; e < ntok * K; e += 256) {
-    const int blk = rows[e];
-    const int t = t0 + tl0 + e / K;
-    if (blk >= 0 && blk <= t / BLK) {
-      const int pos = atomicAdd(&cur[blk], 1);
-      out[pos] = tl0 * K + e;
+  for (int e0 = threadIdx.x; e0 < n; e0 += INV_THREADS * INV_UNROLL) {
+    int blk[INV_UNROLL];
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) {
+      const int e = e0 + u * INV_THREADS;
+      blk[u] = e < n ? rows[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < INV_UNROLL; ++u) {
+      const int e = e0 + u * INV_THREADS;
+      if (blk[u] >= 0 && blk[u] <= (t0 + tl0 + e / K) / BLK) {
+        const int pos = atomicAdd(&cur[blk[u]], 1);
+        out[pos] = tl0 * K + e;
+      }
     }
   }
 }
@@ -126,10 +154,10 @@ hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const 
   const int BG = g.B * g.G;
   const int nchunk = (w.W + INV_CHUNK - 1) / INV_CHUNK;
   const size_t lds = (size_t)g.N * sizeof(int32_t);
-  k_inv_count<<<dim3(nchunk, BG), 256, lds, st>>>(idx, ib.counts, g.T, g.N, g.K, w.t0, w.W, nchunk);
+  k_inv_count<<<dim3(nchunk, BG), INV_THREADS, lds, st>>>(idx, ib.counts, g.T, g.N, g.K, w.t0, w.W, nchunk);
   k_inv_colscan<<<dim3((g.N + 255) / 256, BG), 256, 0, st>>>(ib.counts, ib.len, g.N, nchunk);
   k_inv_blockscan<<<BG, 1024, 0, st>>>(ib.len, ib.base, ib.items, ib.item_count, g.N, ib.max_items, item_tokens);
-  k_inv_scatter<<<dim3(nchunk, BG), 256, lds, st>>>(idx, ib.counts, ib.base, ib.list, g.T, g.N, g.K, w.t0, w.W,
+  k_inv_scatter<<<dim3(nchunk, BG), INV_THREADS, lds, st>>>(idx, ib.counts, ib.base, ib.list, g.T, g.N, g.K, w.t0, w.W,
                                                      nchunk);
   return hipGetLastError();
 }
