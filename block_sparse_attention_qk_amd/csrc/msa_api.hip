@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <cstring>
 
 #include "msa.h"
 #include "msa_internal.h"
@@ -210,6 +211,25 @@ void timing_end(int id, hipStream_t st) {
     if (e_ != hipSuccess) return MSA_ERR_HIP;        \
   } while (0)
 
+// Cache check, on when MSA_VALIDATE is set to a non-empty value other than "0".
+bool validate_on() {
+  const char* e = std::getenv("MSA_VALIDATE");
+  return e && e[0] && std::strcmp(e, "0") != 0;
+}
+
+// Runs the device check of idx (its result in the first 16 bytes of ws) and
+// waits for it: MSA_ERR_INDEX if a row fails.
+msa_status check_cache(const Geo& g, const int32_t* idx, void* ws, hipStream_t st) {
+  if (!validate_on()) return MSA_OK;
+  int32_t* flag = static_cast<int32_t*>(ws);
+  MSA_TRY(launch_fill_zero(reinterpret_cast<float*>(flag), 4, st));
+  MSA_TRY(launch_check_idx(g, idx, flag, st));
+  int32_t h = 0;
+  MSA_TRY(hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, st));
+  MSA_TRY(hipStreamSynchronize(st));
+  return h ? MSA_ERR_INDEX : MSA_OK;
+}
+
 }  // namespace
 }  // namespace msa
 
@@ -294,6 +314,7 @@ msa_status msa_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   W = std::min(W, fwd_window_cap(g));
   const Layout L = layout(g, MSA_OP_FWD, W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (const msa_status c = check_cache(g, idx, ws, st); c != MSA_OK) return c;
   char* base = static_cast<char*>(ws);
   const InvBufs ib = inv_bufs(L, base);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
@@ -321,6 +342,7 @@ msa_status msa_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, c
   if (W == 0) return MSA_ERR_WORKSPACE;
   const Layout L = layout(g, MSA_OP_BWD, W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (const msa_status c = check_cache(g, idx, ws, st); c != MSA_OK) return c;
   char* base = static_cast<char*>(ws);
   const InvBufs ib = inv_bufs(L, base);
   float* Dd = reinterpret_cast<float*>(base + L.Dd);
@@ -357,6 +379,7 @@ msa_status msa_fwd_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* 
   W = std::min(W, fwd_window_cap(g));
   const Layout L = layout(g, MSA_OP_FWD_BWD, W);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (const msa_status c = check_cache(g, idx, ws, st); c != MSA_OK) return c;
   char* base = static_cast<char*>(ws);
   const InvBufs ib = inv_bufs(L, base);
   InvBufs ib2 = ib;  // same list, backward-sized items
@@ -432,6 +455,7 @@ const char* msa_status_str(msa_status s) {
     case MSA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_HIP: return "HIP runtime error";
+    case MSA_ERR_INDEX: return "block-index cache fails the MSA_VALIDATE check";
   }
   return "unknown status";
 }

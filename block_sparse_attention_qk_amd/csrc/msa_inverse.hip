@@ -142,6 +142,48 @@ __global__ __launch_bounds__(INV_THREADS) void k_inv_scatter(const int32_t* __re
   }
 }
 
+// Check of a block-index cache, one wave per row (b, g, t): every entry is -1
+// or a causal block 0..t/128, no block appears twice (an LDS bitmap of the
+// row's blocks, N <= 8192 bits), and at least one entry is a block.  A failing
+// row writes 1 to flag[0]; flag[0] must be 0 before the launch.
+constexpr int CHK_WAVES = 4;
+constexpr int CHK_WORDS = 8192 / 32;
+
+__global__ __launch_bounds__(64 * CHK_WAVES) void k_check_idx(const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ flag, int T, int K,
+                                                             long long rows) {
+  __shared__ uint32_t seen[CHK_WAVES][CHK_WORDS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * CHK_WAVES + wave;
+  if (row >= rows) return;  // whole wave: no workgroup barrier below
+  const int last = (int)(row % T) / BLK;
+  uint32_t* bm = seen[wave];
+  for (int i = lane; i <= last / 32; i += 64) bm[i] = 0;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's clears land before its bitmap updates
+  const int32_t* r = idx + row * K;
+  bool bad = false, any = false;
+  for (int p = lane; p < K; p += 64) {
+    const int e = r[p];
+    if (e == -1) continue;
+    if (e < 0 || e > last) {
+      bad = true;
+      continue;
+    }
+    any = true;
+    const uint32_t bit = 1u << (e & 31);
+    if (atomicOr(&bm[e >> 5], bit) & bit) bad = true;
+  }
+  const bool row_any = __ballot(any) != 0ull;
+  if (bad || (lane == 0 && !row_any)) flag[0] = 1;
+}
+
+hipError_t launch_check_idx(const Geo& g, const int32_t* idx, int32_t* flag, hipStream_t st) {
+  if (g.N > 8192) return hipErrorInvalidValue;
+  const long long rows = (long long)g.B * g.G * g.T;
+  k_check_idx<<<(unsigned)((rows + CHK_WAVES - 1) / CHK_WAVES), 64 * CHK_WAVES, 0, st>>>(idx, flag, g.T, g.K, rows);
+  return hipGetLastError();
+}
+
 int inv_max_items(const Geo& g, int W, int item_tokens) {
   const long long pairs = (long long)W * g.K;
   long long m = g.N + pairs / item_tokens + 1;

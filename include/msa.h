@@ -49,6 +49,15 @@
  *   - Argument checks happen on the host before anything is enqueued; a
  *     failing check returns an error code and enqueues nothing.  A launch
  *     failure returns MSA_ERR_HIP.  Outputs are fully overwritten.
+ *   - Cache check: when the environment variable MSA_VALIDATE is set to a
+ *     non-empty value other than "0" (read at every call), msa_fwd, msa_bwd
+ *     and msa_fwd_bwd first check idx on the device: every entry must be -1
+ *     or a causal block 0..t/128, no block may appear twice in a row, and
+ *     every row must list at least one block.  The call then waits for the
+ *     stream (the check's result is read back to the host) and returns
+ *     MSA_ERR_INDEX without launching anything else if a row fails; the first
+ *     16 bytes of ws are used for the result.  Off by default: unchecked calls
+ *     never synchronise.
  *   - Supported shapes: B >= 1; T >= 128 with T % 128 == 0; H % G == 0 with
  *     R = H / G in {1, 2, 4, 8, 16}; d in {64, 128}; dp in {32, 64, 128};
  *     1 <= topk <= 1024 (topk may exceed the number of causal blocks);
@@ -73,7 +82,8 @@ typedef enum {
   MSA_ERR_UNSUPPORTED = 3, /* a head dim / proxy dim / group ratio not built */
   MSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   MSA_ERR_WORKSPACE = 5,   /* ws_bytes below msa_workspace_min_bytes */
-  MSA_ERR_HIP = 6          /* the HIP runtime reported an error */
+  MSA_ERR_HIP = 6,         /* the HIP runtime reported an error */
+  MSA_ERR_INDEX = 7        /* MSA_VALIDATE set: idx is not a valid cache (nothing else ran) */
 } msa_status;
 
 typedef struct {

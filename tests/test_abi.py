@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib, msa):
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = lib.msa_status_str(code)
         assert s and s.decode() not in seen
         seen.add(s.decode())
