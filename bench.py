@@ -23,6 +23,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern,me
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -283,6 +284,31 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
 DECODE_BATCH = 16  # sequences per decode step, each at the workload's full context
 
 
+def run_dense_context(steps: int) -> dict:
+    """Dense context: the same path with topk = N (every causal block selected,
+    i.e. dense causal GQA attention) next to the sparse configuration, at 16K
+    and 128K tokens; the sparse/dense ratio of the fwd+bwd time shows how the
+    sparse advantage grows with sequence length."""
+    out = {"what": "fwd+bwd (cached indices) of the sparse configuration and of the same shapes at topk = N "
+                   "(dense causal through the same kernels); flops count every selected 128-key block",
+           "runs": []}
+    for name in ("16k", "128k"):
+        sparse = synth.CONFIGS[name]
+        dense = dataclasses.replace(sparse, name=name + "-dense", topk=sparse.N)
+        row = {"T": sparse.T}
+        for tag, c in (("sparse", sparse), ("dense", dense)):
+            r = run_workload(c, steps, 1, host_inputs=False)
+            ms = r["phases_ms"]["fwd"] + r["phases_ms"]["bwd"]
+            row[tag] = {"topk": c.topk, "pairs": r["pairs"], "fwd_bwd_ms": ms,
+                        "fwd_bwd_effective_tflops": r["fwd_bwd_effective_tflops"],
+                        "kernels_ms_per_step": {k: v for k, v in r["kernels_ms_per_step"].items() if v}}
+        row["dense_over_sparse_time"] = row["dense"]["fwd_bwd_ms"] / row["sparse"]["fwd_bwd_ms"]
+        out["runs"].append(row)
+        print("bench: dense context %s: sparse %.1f ms, dense %.1f ms" % (
+            name, row["sparse"]["fwd_bwd_ms"], row["dense"]["fwd_bwd_ms"]), file=sys.stderr, flush=True)
+    return out
+
+
 def run_decode(cfg: synth.Config, B: int, steps: int, warmup: int) -> dict:
     """One decode step = msa_decode_select + msa_decode_fwd for B sequences whose
     caches hold cfg.T tokens (the new one last)."""
@@ -396,10 +422,17 @@ def cpu_baseline(cfg: synth.Config, target_s: float = 15.0) -> dict:
     t_pilot = run(pilot_rows)
     n = int(min(4096, max(pilot_rows, pilot_rows * target_s / max(t_pilot, 1e-3))))
     t = run(n)
+    # the same kind of sample on one thread, about a third of the time budget
+    oracle.set_threads(1)
+    n1 = int(max(8, min(n, (n / t) / cores * (target_s / 3))))
+    t1 = run(n1)
+    oracle.set_threads(cores)
     return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": ("%d query tokens drawn uniformly from the %s workload: Index Branch rows, forward rows and "
                        "backward dQ rows over all heads and groups (the oracle's dK/dV pass is not in the sample); "
-                       "%.1f s on %d threads" % (n, cfg.name, t, cores))}
+                       "%.1f s on %d threads" % (n, cfg.name, t, cores)),
+            "single_thread": {"value": n1 / t1, "unit": "tokens/s", "cores": 1,
+                              "sample": "%d query tokens of the same kind; %.1f s on 1 thread" % (n1, t1)}}
 
 
 def main() -> int:
@@ -408,11 +441,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--also", default="1m,pattern,merged,decode",
+    ap.add_argument("--also", default="1m,pattern,merged,decode,dense",
                     help="comma list of extra workloads: config names, 'pattern' (the main config with the fixed "
                          "window/dilation pattern united with the proxy top-k), 'merged' (the main config through "
-                         "msa_fwd_bwd), 'decode' (decode steps of %d sequences at the main config's full context); "
-                         "'' for none" % DECODE_BATCH)
+                         "msa_fwd_bwd), 'decode' (decode steps of %d sequences at the main config's full context), "
+                         "'dense' (16K and 128K at topk = N beside their sparse configurations); '' for none"
+                         % DECODE_BATCH)
     ap.add_argument("--also-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -454,6 +488,7 @@ def main() -> int:
     main_res = run_workload(cfg, args.steps, args.warmup, host_inputs=not args.gpu_inputs)
     print("bench: main workload done: %.3f ms/step" % main_res["ms_per_step"], file=sys.stderr, flush=True)
     extra = []
+    dense_context = None
     for name in [s for s in args.also.split(",") if s and s != args.config]:
         if name == "pattern":
             print("bench: extra workload %s + pattern %s" % (cfg, PATTERN), file=sys.stderr, flush=True)
@@ -464,6 +499,10 @@ def main() -> int:
             print("bench: extra workload %s, merged fwd+bwd" % (cfg,), file=sys.stderr, flush=True)
             extra.append(run_workload(cfg, args.steps, 2, host_inputs=False, merged=True))
             print("bench: merged done: %.1f ms/step" % extra[-1]["ms_per_step"], file=sys.stderr, flush=True)
+            continue
+        if name == "dense":
+            print("bench: dense context (topk = N) at 16K and 128K", file=sys.stderr, flush=True)
+            dense_context = run_dense_context(args.also_steps)
             continue
         if name == "decode":
             print("bench: decode steps, %d sequences of %s" % (DECODE_BATCH, cfg), file=sys.stderr, flush=True)
@@ -504,6 +543,8 @@ def main() -> int:
         "kernels_ms_per_step": main_res["kernels_ms_per_step"],
         "workloads": [main_res] + extra,
     }
+    if dense_context is not None:
+        line["dense_context"] = dense_context
     print(json.dumps(line))
     return 0
 
