@@ -406,7 +406,10 @@ __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ 
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
+  // slots per batch: independent loads in flight per thread.  32 covers a whole
+  // row of topk 32 in one batch: two waves per SIMD issuing 32 loads each keep
+  // more bytes in flight than seven waves issuing 8.
+  constexpr int SB = 32;
   for (int s0 = 0; s0 < K; s0 += SB) {
     // entries and partial rows of the batch are loaded together; slots past K
     // re-read the last one and slots without a partial are masked after the load

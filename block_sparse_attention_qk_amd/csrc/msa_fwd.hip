@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   // entries, lse and partial rows together (slots past K re-read the last one;
   // a slot without a partial is read and then masked, so no load waits on a
   // branch), and the accumulator is rescaled when the maximum grows.
-  constexpr int SB = 8;  // slots per batch: independent loads in flight per thread
+  constexpr int SB = 16;  // slots per batch: independent loads in flight per thread
   float M = -INFINITY, L = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
