@@ -255,6 +255,16 @@ def test_1m_config_gpu_generated(msa, oracle_mod):
     _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=128, blocks_from_end=[0, 1])
 
 
+def test_max_topk_dense_128k_gpu_generated(msa, oracle_mod):
+    """topk = 1024, the largest the boundary takes: at T = 131072 every query
+    selects every causal block (dense causal attention through the sparse
+    kernels).  Block 0 is then picked by all 131072 tokens, so its backward
+    list is cut into 32 items whose dK/dV are added atomically.  Checked on
+    sampled rows and on late key blocks against the oracle."""
+    cfg = synth.Config("128k-topk1024", 1, 131072, 8, 1, 128, 64, 1024)
+    _gpu_generated_check(msa, oracle_mod, cfg, n_rows=32, blocks_from_end=[0, 1], seed=2)
+
+
 @pytest.mark.parametrize("T,topk", [(1 << 18, 40), (1 << 20, 288)])
 def test_long_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     """Rows longer than 1024 blocks go through the radix select.  A proxy-key
