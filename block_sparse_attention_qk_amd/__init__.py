@@ -165,10 +165,29 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
+def _same_device(device, *named) -> None:
+    """Every tensor of a call must live on the device of its first input."""
+    for t, name in named:
+        if t is not None and t.device != device:
+            raise ValueError("%s is on %s, the call's inputs on %s" % (name, t.device, device))
+
+
+def _out(t: torch.Tensor, name: str, dtype, shape, device) -> torch.Tensor:
+    """A caller-provided output: the kernels write exactly `shape` elements into it."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    _same_device(device, (t, name))
+    return t
+
+
 def _ws(ws: Optional[Workspace], device, nbytes: int) -> torch.Tensor:
     if ws is None:
         return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
-    return ws.get(nbytes)
+    buf = ws.get(nbytes)
+    if buf.device != device:
+        raise ValueError("workspace is on %s, the call's inputs on %s" % (buf.device, device))
+    return buf
 
 
 def msa_proxy_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, ws: Optional[Workspace] = None,
@@ -179,13 +198,16 @@ def msa_proxy_select(qp: torch.Tensor, kp: torch.Tensor, topk: int, ws: Optional
     if qp.shape != kp.shape:
         raise ValueError("qp and kp shapes differ: %s vs %s" % (tuple(qp.shape), tuple(kp.shape)))
     B, T, G, dp = qp.shape
+    _same_device(qp.device, (kp, "kp"))
     dims = _dims(B, T, G, G, 64, dp, topk, 0.0)
     lib = load()
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_SELECT)
     if nbytes == 0:
         _check(2)
-    idx = out if out is not None else torch.empty((B, G, T, topk), dtype=torch.int32, device=qp.device)
-    _need(idx, "idx", torch.int32, 4)
+    if out is not None:
+        idx = _out(out, "out", torch.int32, (B, G, T, topk), qp.device)
+    else:
+        idx = torch.empty((B, G, T, topk), dtype=torch.int32, device=qp.device)
     w = _ws(ws, qp.device, nbytes)
     _check(lib.msa_proxy_select(ctypes.byref(dims), _ptr(qp), _ptr(kp), _ptr(idx), _ptr(w), w.numel(),
                                 _stream(qp.device)))
@@ -214,7 +236,8 @@ def msa_pattern_select(B: int, T: int, G: int, window: int, dilation: int, idx_i
         width = pattern_width(T, window, dilation, k_in)
     if out is None:
         out = torch.empty((B, G, T, width), dtype=torch.int32, device=device if device is not None else "cuda")
-    _need(out, "out", torch.int32, 4)
+    else:
+        _out(out, "out", torch.int32, (B, G, T, width), idx_in.device if idx_in is not None else out.device)
     dims = _dims(B, T, G, G, 64, 32, width, 0.0)
     _check(load().msa_pattern_select(ctypes.byref(dims), int(window), int(dilation),
                                      _ptr(idx_in) if idx_in is not None else None, int(k_in), _ptr(out),
@@ -242,6 +265,7 @@ def msa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor
     if v.shape != k.shape:
         raise ValueError("v shape %s differs from k shape %s" % (tuple(v.shape), tuple(k.shape)))
     dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    _same_device(q.device, (k, "k"), (v, "v"), (idx, "idx"))
     lib = load()
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_FWD)
     if nbytes == 0:
@@ -250,7 +274,8 @@ def msa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor
         o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=q.device)
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o = _out(out[0], "out[0] (o)", torch.bfloat16, (B, T, H, d), q.device)
+        lse = _out(out[1], "out[1] (lse)", torch.float32, (B, T, H), q.device)
     w = _ws(ws, q.device, nbytes)
     _check(lib.msa_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(o), _ptr(lse), _ptr(w),
                        w.numel(), _stream(q.device)))
@@ -268,6 +293,7 @@ def msa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, 
     if v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or lse.shape != q.shape[:3]:
         raise ValueError("inconsistent shapes for msa_bwd")
     dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    _same_device(q.device, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse"), (idx, "idx"))
     lib = load()
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_BWD)
     if nbytes == 0:
@@ -277,7 +303,9 @@ def msa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, 
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
     else:
-        dq, dk, dv = out
+        dq = _out(out[0], "out[0] (dq)", torch.bfloat16, tuple(q.shape), q.device)
+        dk = _out(out[1], "out[1] (dk)", torch.bfloat16, tuple(k.shape), q.device)
+        dv = _out(out[2], "out[2] (dv)", torch.bfloat16, tuple(k.shape), q.device)
     w = _ws(ws, q.device, nbytes)
     _check(lib.msa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(idx),
                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
@@ -294,6 +322,7 @@ def msa_fwd_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.T
     if v.shape != k.shape or dout.shape != q.shape:
         raise ValueError("inconsistent shapes for msa_fwd_bwd")
     dims, B, T, H, G, d, topk = _main_dims(q, k, idx, scale)
+    _same_device(q.device, (k, "k"), (v, "v"), (dout, "dout"), (idx, "idx"))
     lib = load()
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_FWD_BWD)
     if nbytes == 0:
@@ -303,7 +332,11 @@ def msa_fwd_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.T
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
-        o, lse, dq, dk, dv = out
+        o = _out(out[0], "out[0] (o)", torch.bfloat16, tuple(q.shape), q.device)
+        lse = _out(out[1], "out[1] (lse)", torch.float32, (B, T, H), q.device)
+        dq = _out(out[2], "out[2] (dq)", torch.bfloat16, tuple(q.shape), q.device)
+        dk = _out(out[3], "out[3] (dk)", torch.bfloat16, tuple(k.shape), q.device)
+        dv = _out(out[4], "out[4] (dv)", torch.bfloat16, tuple(k.shape), q.device)
     w = _ws(ws, q.device, nbytes)
     _check(lib.msa_fwd_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(idx), _ptr(o), _ptr(lse),
                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream(q.device)))
@@ -334,8 +367,11 @@ def msa_decode_select(qp: torch.Tensor, kp: torch.Tensor, lens: torch.Tensor, to
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_SELECT)
     if nbytes == 0:
         _check(2)
-    idx = out if out is not None else torch.empty((B, G, topk), dtype=torch.int32, device=qp.device)
-    _need(idx, "idx", torch.int32, 3)
+    _same_device(qp.device, (kp, "kp"))
+    if out is not None:
+        idx = _out(out, "out", torch.int32, (B, G, topk), qp.device)
+    else:
+        idx = torch.empty((B, G, topk), dtype=torch.int32, device=qp.device)
     w = _ws(ws, qp.device, nbytes)
     _check(lib.msa_decode_select(ctypes.byref(dims), _ptr(qp), _ptr(kp), _ptr(lens), _ptr(idx), _ptr(w), w.numel(),
                                  _stream(qp.device)))
@@ -359,6 +395,7 @@ def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torc
     if idx.shape[0] != B or idx.shape[1] != G:
         raise ValueError("idx shape %s does not match [B,G,topk] = [%d,%d,*]" % (tuple(idx.shape), B, G))
     _lens(lens, B, q.device)
+    _same_device(q.device, (k, "k"), (v, "v"), (idx, "idx"))
     dims = _dims(B, T, H, G, d, 32, idx.shape[2], scale)
     lib = load()
     nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_FWD)
@@ -368,7 +405,8 @@ def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torc
         o = torch.empty((B, H, d), dtype=torch.bfloat16, device=q.device)
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     else:
-        o, lse = out
+        o = _out(out[0], "out[0] (o)", torch.bfloat16, (B, H, d), q.device)
+        lse = _out(out[1], "out[1] (lse)", torch.float32, (B, H), q.device)
     w = _ws(ws, q.device, nbytes)
     _check(lib.msa_decode_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(idx), _ptr(o),
                               _ptr(lse), _ptr(w), w.numel(), _stream(q.device)))
