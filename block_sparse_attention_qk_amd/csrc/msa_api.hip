@@ -128,10 +128,11 @@ bool is_pow2_le16(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 1
 msa_status make_geo(const msa_dims* d, msa_op op, Geo* g) {
   if (!d) return MSA_ERR_NULL;
   if (d->B < 1 || d->T < 128 || d->T % 128 != 0 || d->T > (1 << 20) || d->G < 1 || d->topk < 1 ||
-      d->topk > 1024 || std::isnan(d->scale))
+      d->topk > 1024 || !std::isfinite(d->scale))
     return MSA_ERR_SHAPE;
   if ((int64_t)d->T * d->topk >= ((int64_t)1 << 31) || (int64_t)d->B * d->T >= ((int64_t)1 << 30))
     return MSA_ERR_SHAPE;
+  if ((int64_t)d->B * d->G > 65535) return MSA_ERR_SHAPE;  // (batch, group) is a grid dimension
   g->B = d->B; g->T = d->T; g->G = d->G; g->K = d->topk; g->N = d->T / 128;
   g->H = d->H; g->D = d->d; g->DP = d->dp;
   if (op == MSA_OP_SELECT) {
@@ -148,12 +149,9 @@ msa_status make_geo(const msa_dims* d, msa_op op, Geo* g) {
 
 bool is_decode(msa_op op) { return op == MSA_OP_DECODE_SELECT || op == MSA_OP_DECODE_FWD; }
 
-// Decode geometry: the training checks plus a grid bound on B*G (grid y).
+// Decode geometry: the training checks.
 msa_status make_dec_geo(const msa_dims* d, msa_op op, Geo* g) {
-  const msa_status s = make_geo(d, op == MSA_OP_DECODE_SELECT ? MSA_OP_SELECT : MSA_OP_FWD, g);
-  if (s != MSA_OK) return s;
-  if ((int64_t)d->B * d->G > 65535) return MSA_ERR_SHAPE;
-  return MSA_OK;
+  return make_geo(d, op == MSA_OP_DECODE_SELECT ? MSA_OP_SELECT : MSA_OP_FWD, g);
 }
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

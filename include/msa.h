@@ -61,7 +61,7 @@
  *   - Supported shapes: B >= 1; T >= 128 with T % 128 == 0; H % G == 0 with
  *     R = H / G in {1, 2, 4, 8, 16}; d in {64, 128}; dp in {32, 64, 128};
  *     1 <= topk <= 1024 (topk may exceed the number of causal blocks);
- *     T * topk < 2^31.
+ *     T * topk < 2^31; B * T < 2^30; B * G <= 65535; scale finite.
  */
 #ifndef MSA_H
 #define MSA_H

@@ -67,6 +67,8 @@ def test_status_strings(lib):
     (dict(H=64, G=2), ERR_UNSUP),        # R = 32
     (dict(d=96), ERR_UNSUP),
     (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(scale=float("inf")), ERR_SHAPE),
+    (dict(B=256, G=256, H=256, T=128), ERR_SHAPE),  # B*G above the grid's 65535
 ])
 def test_main_branch_rejects_bad_dims(lib, msa, kw, code):
     d = _dims(msa, **kw)
@@ -82,6 +84,7 @@ def test_main_branch_rejects_bad_dims(lib, msa, kw, code):
     (dict(dp=256), ERR_UNSUP),
     (dict(T=200), ERR_SHAPE),
     (dict(G=0), ERR_SHAPE),
+    (dict(B=2, G=40000, H=40000, T=128), ERR_SHAPE),
 ])
 def test_select_rejects_bad_dims(lib, msa, kw, code):
     d = _dims(msa, **kw)
