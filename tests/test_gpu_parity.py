@@ -185,7 +185,7 @@ def test_16k_config_sampled(msa, oracle_mod):
 
 def test_128k_config_sampled(msa, oracle_mod):
     cfg = synth.CONFIGS["128k"]
-    _sampled_check(msa, oracle_mod, cfg, n_rows=512, blocks_per_group=[cfg.N // 2, cfg.N - 3, cfg.N - 1])
+    _sampled_check(msa, oracle_mod, cfg, n_rows=1024, blocks_per_group=[cfg.N // 2, cfg.N - 3, cfg.N - 1])
 
 
 def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
@@ -248,11 +248,11 @@ def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
 
 
 def test_512k_config_gpu_generated(msa, oracle_mod):
-    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["512k"], n_rows=256, blocks_from_end=[0, 2])
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["512k"], n_rows=1024, blocks_from_end=[0, 2])
 
 
 def test_1m_config_gpu_generated(msa, oracle_mod):
-    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=128, blocks_from_end=[0, 1])
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=1024, blocks_from_end=[0, 1])
 
 
 def test_max_topk_dense_128k_gpu_generated(msa, oracle_mod):
