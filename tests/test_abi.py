@@ -249,3 +249,13 @@ def test_fwd_bwd_checks(lib, msa):
     for kw, code in ((dict(H=6, G=2), ERR_UNSUP), (dict(T=1000), ERR_SHAPE), (dict(d=96), ERR_UNSUP)):
         bad = _dims(msa, **kw)
         assert f(ctypes.byref(bad), *([P] * 11), 1 << 40, None) == code, kw
+
+
+def test_missing_library_fails_loudly(msa, monkeypatch, tmp_path):
+    """Without the built library the binding raises: there is no fallback path."""
+    monkeypatch.setattr(msa, "_lib", None)
+    monkeypatch.setattr(msa, "_LIB_PATH", str(tmp_path / "libmsa.so"))
+    with pytest.raises(msa.MsaError):
+        msa.load()
+    with pytest.raises(msa.MsaError):
+        msa.msa_workspace_bytes(1, 1024, 8, 2, 128, 64, 4, msa.OP_FWD)
