@@ -9,6 +9,13 @@ Array conventions (all row-major):
   idx:    [B, G, T, topk] int32, ascending block ids, -1 padded
 Inputs may be torch tensors (any float dtype, bf16 included) or numpy arrays;
 they are converted to float64 before the call, which is exact for bf16.
+
+Parity unpinned against the pages: the pages print no worked example or
+reference value for any part of the method.  select, fwd and bwd are pinned
+by the mathematics instead (brute force, closed forms, invariants, library
+routines and finite differences; tests/test_oracle_*.py and tests/golden/).
+pattern_select, decode_select and decode_fwd follow readings of pages that
+define neither, so beyond those pins they are parity unpinned.
 """
 from __future__ import annotations
 
@@ -220,6 +227,9 @@ def pattern_select(B: int, T: int, G: int, window: int, dilation: int, width: in
     below the window whose index is a multiple of `dilation` (none when 0), and
     the causal entries of idx_in[b, g, t, :]; the rest of the row is -1.
     Plain per-row set construction (test infrastructure only).
+    Parity unpinned against the pages (they give no example of the pattern):
+    pinned by hand-worked rows, cases that must select every causal block, the
+    empty pattern, and an independent boolean-mask formulation.
     """
     out = np.full((B, G, T, width), -1, dtype=np.int32)
     ii = None if idx_in is None else _i32(idx_in)
@@ -255,7 +265,8 @@ def decode_select(dm: Dims, qp, kp, lens):
     of capacity dm.T).  The row is selected exactly as a training row (select()
     on that prefix).  Returns (idx [B,G,topk] int32, pooled [B,G,T/128] fp32,
     -inf past the causal blocks); sequences with lens outside 1..T give an all -1
-    row and -inf scores."""
+    row and -inf scores.  Parity unpinned against the pages (no decode example
+    is printed): pinned to the training rows and a hand-built ranking."""
     qp64, kp64 = _f64(qp), _f64(kp)
     ln = _decode_len(lens, dm.B, dm.T)
     N = (dm.T + BLOCK - 1) // BLOCK
@@ -281,7 +292,9 @@ def decode_fwd(dm: Dims, q, k, v, lens, idx):
     idx[b] ([B,G,topk]) exactly as fwd() does for a training row (one call per
     group).  Entries that are -1 or above t/128 are dropped first.  Returns
     (o [B,H,d], lse [B,H]) in float64; a group whose row keeps no entry, or a
-    sequence with lens outside 1..T, gives o = 0, lse = -inf."""
+    sequence with lens outside 1..T, gives o = 0, lse = -inf.  Parity unpinned
+    against the pages (no decode example is printed): pinned to a plain float64
+    softmax over the prefix and to the training rows."""
     q64, k64, v64 = _f64(q), _f64(k), _f64(v)
     ix = _i32(idx)
     ln = _decode_len(lens, dm.B, dm.T)
