@@ -42,8 +42,8 @@ _lib = None
 
 OP_SELECT, OP_FWD, OP_BWD, OP_DECODE_SELECT, OP_DECODE_FWD, OP_FWD_BWD = 0, 1, 2, 3, 4, 5
 EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_pattern_select",
-                    "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select", "msa_decode_fwd", "msa_status_str",
-                    "msa_version", "msa_timing_enable", "msa_timing_read")
+                    "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select", "msa_decode_fwd",
+                    "msa_status_str", "msa_version", "msa_timing_enable", "msa_timing_read")
 
 # msa_kernel_id values (include/msa.h)
 KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
@@ -378,11 +378,7 @@ def msa_decode_select(qp: torch.Tensor, kp: torch.Tensor, lens: torch.Tensor, to
     return idx
 
 
-def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, idx: torch.Tensor,
-                   scale: float = 0.0, ws: Optional[Workspace] = None,
-                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
-    """Decode-step Main Branch: q [B,H,d] (the new tokens), k/v caches [B,T,G,d],
-    lens [B] int32, idx [B,G,topk] -> (o [B,H,d] bf16, lse [B,H] fp32)."""
+def _decode_fwd_args(q, k, v, lens, idx, scale, out):
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -397,8 +393,7 @@ def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torc
     _lens(lens, B, q.device)
     _same_device(q.device, (k, "k"), (v, "v"), (idx, "idx"))
     dims = _dims(B, T, H, G, d, 32, idx.shape[2], scale)
-    lib = load()
-    nbytes = lib.msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_FWD)
+    nbytes = load().msa_workspace_bytes(ctypes.byref(dims), OP_DECODE_FWD)
     if nbytes == 0:
         _check(2)
     if out is None:
@@ -407,7 +402,17 @@ def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torc
     else:
         o = _out(out[0], "out[0] (o)", torch.bfloat16, (B, H, d), q.device)
         lse = _out(out[1], "out[1] (lse)", torch.float32, (B, H), q.device)
+    return dims, nbytes, o, lse
+
+
+def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, idx: torch.Tensor,
+                   scale: float = 0.0, ws: Optional[Workspace] = None,
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Decode-step Main Branch: q [B,H,d] (the new tokens), k/v caches [B,T,G,d],
+    lens [B] int32, idx [B,G,topk] -> (o [B,H,d] bf16, lse [B,H] fp32)."""
+    dims, nbytes, o, lse = _decode_fwd_args(q, k, v, lens, idx, scale, out)
     w = _ws(ws, q.device, nbytes)
-    _check(lib.msa_decode_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(idx), _ptr(o),
-                              _ptr(lse), _ptr(w), w.numel(), _stream(q.device)))
+    _check(load().msa_decode_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(idx), _ptr(o),
+                                 _ptr(lse), _ptr(w), w.numel(), _stream(q.device)))
     return o, lse
+

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 
 #include "msa.h"
 #include "msa_internal.h"
@@ -156,6 +157,17 @@ msa_status make_dec_geo(const msa_dims* d, msa_op op, Geo* g) {
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The integer a caller passed for an enum argument.  C callers may pass any
+// int; reading it through the object representation keeps values outside the
+// enumerators defined (they select the "unknown" branches).
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enums of the ABI are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 InvBufs inv_bufs(const Layout& L, char* ws) {
   InvBufs ib;
   ib.counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -173,7 +185,10 @@ InvBufs inv_bufs(const Layout& L, char* ws) {
     if ((x) != hipSuccess) return MSA_ERR_HIP;      \
   } while (0)
 
-// ---- opt-in launch timing (process-wide; see msa_timing_enable)
+// ---- opt-in launch timing.  The state belongs to the calling host thread
+// (created by its first msa_timing_enable, kept until the process ends), so
+// calls from different threads never share it; with timing off a launch only
+// reads this thread's null pointer.
 constexpr int MAX_TIMED = 4096;
 struct TimedLaunch {
   hipEvent_t a = nullptr, b = nullptr;
@@ -184,20 +199,21 @@ struct TimingState {
   int n = 0;
   TimedLaunch slot[MAX_TIMED];
 };
-TimingState g_timing;
+thread_local TimingState* t_timing = nullptr;
 
 int timing_begin(int kernel, hipStream_t st) {
-  if (!g_timing.on || g_timing.n >= MAX_TIMED) return -1;
-  TimedLaunch& s = g_timing.slot[g_timing.n];
+  TimingState* ts = t_timing;
+  if (!ts || !ts->on || ts->n >= MAX_TIMED) return -1;
+  TimedLaunch& s = ts->slot[ts->n];
   if (!s.a && hipEventCreate(&s.a) != hipSuccess) return -1;
   if (!s.b && hipEventCreate(&s.b) != hipSuccess) return -1;
   if (hipEventRecord(s.a, st) != hipSuccess) return -1;
   s.kernel = kernel;
-  return g_timing.n++;
+  return ts->n++;
 }
 
 void timing_end(int id, hipStream_t st) {
-  if (id >= 0) (void)hipEventRecord(g_timing.slot[id].b, st);
+  if (id >= 0) (void)hipEventRecord(t_timing->slot[id].b, st);
 }
 
 // Launch `call` (a hipError_t expression), timed as `kernel` when timing is on.
@@ -235,7 +251,10 @@ using namespace msa;
 
 extern "C" {
 
-size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
+size_t msa_workspace_bytes(const msa_dims* dims, msa_op op_in) {
+  const int opv = enum_value(op_in);
+  if (opv < MSA_OP_SELECT || opv > MSA_OP_FWD_BWD) return 0;
+  const msa_op op = static_cast<msa_op>(opv);
   Geo g;
   if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
   if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_FWD_BWD) return 0;
@@ -248,7 +267,10 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op) {
   return layout(g, op, W > 0 ? W : min_window(g)).total;
 }
 
-size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op) {
+size_t msa_workspace_min_bytes(const msa_dims* dims, msa_op op_in) {
+  const int opv = enum_value(op_in);
+  if (opv < MSA_OP_SELECT || opv > MSA_OP_FWD_BWD) return 0;
+  const msa_op op = static_cast<msa_op>(opv);
   Geo g;
   if (is_decode(op)) return make_dec_geo(dims, op, &g) == MSA_OK ? layout(g, op, 0).total : 0;
   if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_FWD_BWD) return 0;
@@ -445,7 +467,7 @@ msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf1
 }
 
 const char* msa_status_str(msa_status s) {
-  switch (s) {
+  switch (enum_value(s)) {
     case MSA_OK: return "ok";
     case MSA_ERR_NULL: return "null pointer argument";
     case MSA_ERR_SHAPE: return "dimensions out of the supported range";
@@ -461,8 +483,13 @@ const char* msa_status_str(msa_status s) {
 const char* msa_version(void) { return "msa-gfx950 0.1"; }
 
 void msa_timing_enable(int on) {
-  g_timing.on = on != 0;
-  g_timing.n = 0;
+  if (!t_timing) {
+    if (!on) return;
+    t_timing = new (std::nothrow) TimingState();
+    if (!t_timing) return;
+  }
+  t_timing->on = on != 0;
+  t_timing->n = 0;
 }
 
 msa_status msa_timing_read(double* ms, int32_t* launches, int32_t n) {
@@ -470,8 +497,9 @@ msa_status msa_timing_read(double* ms, int32_t* launches, int32_t n) {
     if (ms) ms[k] = 0.0;
     if (launches) launches[k] = 0;
   }
-  for (int i = 0; i < g_timing.n; ++i) {
-    const TimedLaunch& s = g_timing.slot[i];
+  const int n_rec = t_timing ? t_timing->n : 0;
+  for (int i = 0; i < n_rec; ++i) {
+    const TimedLaunch& s = t_timing->slot[i];
     float t = 0.f;
     if (hipEventSynchronize(s.b) != hipSuccess || hipEventElapsedTime(&t, s.a, s.b) != hipSuccess)
       return MSA_ERR_HIP;

@@ -223,11 +223,12 @@ msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf1
 /* ---- Optional launch timing, for benchmarks and profiling tools.
  * When enabled, the library records a pair of HIP events on the call's stream
  * around every launch of the kernels listed below (the inverse-index build
- * counts as one launch of four kernels).  Timing state is process-wide and
- * not thread-safe; it is off by default and costs nothing when off.  At most
- * 4096 launches are recorded between two msa_timing_enable calls; later
- * launches run untimed.  Events are created on first use and kept until the
- * process ends. */
+ * counts as one launch of four kernels).  Timing state belongs to the calling
+ * host thread: msa_timing_enable and msa_timing_read act on the launches that
+ * thread made, and threads never share it.  It is off by default and costs
+ * nothing when off.  At most 4096 launches are recorded between two
+ * msa_timing_enable calls; later launches run untimed.  A thread's events are
+ * created on first use and kept until the process ends. */
 typedef enum {
   MSA_K_PROXY_POOL = 0,   /* proxy score + block max-pool */
   MSA_K_TOPK = 1,         /* per-row top-k -> idx */

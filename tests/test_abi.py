@@ -259,3 +259,4 @@ def test_missing_library_fails_loudly(msa, monkeypatch, tmp_path):
         msa.load()
     with pytest.raises(msa.MsaError):
         msa.msa_workspace_bytes(1, 1024, 8, 2, 128, 64, 4, msa.OP_FWD)
+

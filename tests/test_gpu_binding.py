@@ -67,3 +67,20 @@ def test_non_contiguous_out_is_rejected(setup):
     wide = torch.empty((cfg.B, cfg.T, cfg.H, 2 * cfg.d), dtype=torch.bfloat16, device="cuda")[..., ::2]
     with pytest.raises(ValueError):
         m.msa_fwd(x["q"], x["k"], x["v"], idx, out=(wide, torch.empty_like(lse)))
+
+
+def test_launch_timing_belongs_to_the_calling_thread(setup):
+    """Timing state is per host thread: launches made by another thread are
+    neither recorded nor read by this one."""
+    import threading
+    m, cfg, x, idx, o, lse = setup
+    m.timing_enable(True)
+    t = threading.Thread(target=lambda: m.msa_fwd(x["q"], x["k"], x["v"], idx))
+    t.start()
+    t.join()
+    torch.cuda.synchronize()
+    assert all(n == 0 for _, n in m.timing_read().values())
+    m.msa_fwd(x["q"], x["k"], x["v"], idx)
+    rec = m.timing_read()
+    m.timing_enable(False)
+    assert rec["fwd_partials"][1] == 1 and rec["fwd_combine"][1] == 1

@@ -3,12 +3,15 @@
 Every case draws seeded inputs from ``synth``, runs msa_proxy_select, msa_fwd
 and msa_bwd on the GPU, and compares with the oracle: indices bit-exact up to
 near-ties, main branch with the GPU's own indices (shared indices) against
-cos >= 0.999 (tighter than the 0.99 target bar) and max-abs <= 2e-2.
+cos >= 0.999 (tighter than the 0.99 target bar) and, element by element,
+|got - ref| <= 2e-2 plus half a bf16 ulp of the value (the rounding of the
+bf16 outputs; lse is fp32 and gets the plain 2e-2).
 
 Small shapes are checked on every output element.  The 16K and 128K
 configurations run at full size on the GPU and are checked on sampled tokens
 (idx, o, lse, dq depend only on their own row) and sampled key blocks (dk,
-dv, recomputed by the oracle from every pair that selected the block).
+dv, recomputed by the oracle from every pair that selected the block),
+including at 128K blocks whose backward is cut into several work items.
 """
 import numpy as np
 import pytest
@@ -98,7 +101,7 @@ def test_repeated_calls_are_bitwise_reproducible(msa):
     for n in ("idx", "o", "lse", "dq"):
         assert torch.equal(a[n], b[n]), n
     for n in ("dk", "dv"):
-        parity.assert_close(n, a[n], b[n], 0.999999, 2 ** -6)  # max-abs relative to max|b|
+        parity.assert_consistent(n, a[n], b[n], 0.999999, 2 ** -6)
 
 
 def test_custom_scale(msa, oracle_mod):
@@ -150,10 +153,18 @@ def test_small_workspace_walks_windows(msa):
     for n in ("idx", "o", "lse", "dq"):
         assert torch.equal(full[n], small[n]), n
     for n in ("dk", "dv"):
-        parity.assert_close(n, small[n], full[n], 0.99999, 2 ** -7)
+        parity.assert_consistent(n, small[n], full[n], 0.99999, 2 ** -7)
 
 
-def _sampled_check(msa, oracle_mod, cfg, n_rows, blocks_per_group, seed=0):
+# A backward work item holds at most this many pairs; a block selected by more
+# tokens is cut into several items whose dK/dV meet in one accumulator through
+# float atomics.
+BWD_ITEM_PAIRS = 4096
+
+
+def _sampled_check(msa, oracle_mod, cfg, n_rows, blocks_per_group, seed=0, split_blocks=()):
+    """split_blocks: (group, block) pairs that must be cut into several backward
+    items; each is checked on every element of its dK/dV against the oracle."""
     print("sampled case", cfg, flush=True)
     x = synth.make_inputs(cfg, seed_offset=seed)
     r = _gpu_all(msa, x, cfg.topk)
@@ -183,6 +194,14 @@ def _sampled_check(msa, oracle_mod, cfg, n_rows, blocks_per_group, seed=0):
     dv_g = torch.stack([r["dv"][0, (c % N) * 128:(c % N) * 128 + 128, (c // N) % cfg.G] for c in blocks])
     res.append(parity.assert_close("dk_blocks", dk_g, dk_ref, COS))
     res.append(parity.assert_close("dv_blocks", dv_g, dv_ref, COS))
+    for g, blk in split_blocks:
+        readers = int((idx[0, g] == blk).any(axis=1).sum())
+        print("split block g=%d blk=%d: %d selecting tokens" % (g, blk, readers), flush=True)
+        assert readers > BWD_ITEM_PAIRS, (g, blk, readers)
+        dk_ref, dv_ref = oracle_mod.bwd_blocks(dm, f64["q"], f64["k"], f64["v"], f64["dout"], idx, [g * N + blk])
+        sl = slice(blk * 128, blk * 128 + 128)
+        res.append(parity.assert_close("dk_split", r["dk"][0, sl, g][None], dk_ref, COS))
+        res.append(parity.assert_close("dv_split", r["dv"][0, sl, g][None], dv_ref, COS))
     # Global invariants at full size: sum_j dK_j = 0 and sum_j dV_j = sum dO per group.
     R = cfg.H // cfg.G
     dk_sum = r["dk"].double().sum(dim=1)
@@ -190,7 +209,7 @@ def _sampled_check(msa, oracle_mod, cfg, n_rows, blocks_per_group, seed=0):
     do_sum = x["dout"].double().view(cfg.B, cfg.T, cfg.G, R, cfg.d).sum(dim=(1, 3))
     dk_mass = r["dk"].double().abs().sum(dim=1)
     assert (dk_sum.abs() / dk_mass.clamp_min(1e-30)).max().item() < 1e-2
-    parity.assert_close("dv_total", dv_sum, do_sum, 0.99999, 1e-3 * do_sum.abs().max().item())
+    parity.assert_close("dv_total", dv_sum, do_sum, 0.99999, 1e-3 * do_sum.abs().max().item(), bf16_out=False)
     print(res, flush=True)
 
 
@@ -201,7 +220,10 @@ def test_16k_config_sampled(msa, oracle_mod):
 
 def test_128k_config_sampled(msa, oracle_mod):
     cfg = synth.CONFIGS["128k"]
-    _sampled_check(msa, oracle_mod, cfg, n_rows=1024, blocks_per_group=[cfg.N // 2, cfg.N - 3, cfg.N - 1])
+    # block 0 (about 18K selecting tokens per group: five items), block 100 (three)
+    # and block 300 (two) go through the atomically added backward items
+    _sampled_check(msa, oracle_mod, cfg, n_rows=1024, blocks_per_group=[cfg.N // 2, cfg.N - 3, cfg.N - 1],
+                   split_blocks=[(0, 0), (1, 100), (2, 300)])
 
 
 def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
@@ -259,7 +281,8 @@ def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
     res.append(parity.assert_close("dv_blocks", dv_g, dv_ref, COS))
     dv_sum = dv.double().sum(dim=1)
     do_sum = x["dout"].double().view(cfg.B, cfg.T, cfg.G, R, cfg.d).sum(dim=(1, 3))
-    parity.assert_close("dv_total", dv_sum.cpu(), do_sum.cpu(), 0.99999, 1e-3 * do_sum.abs().max().item())
+    parity.assert_close("dv_total", dv_sum.cpu(), do_sum.cpu(), 0.99999, 1e-3 * do_sum.abs().max().item(),
+                        bf16_out=False)
     print(res, flush=True)
 
 
