@@ -391,7 +391,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_attn(const bf16raw* __re
 // max of the valid slots' lse, then every lane adds the weighted partials of
 // its D/64 value columns over its wave's slots (the loads do not depend on each
 // other), and the NW sums meet in LDS.  Rows with no valid slot (length
-// outside 1..T) get o = 0 and lse = -inf.
+// outside 1..T) get o = 0 and lse = -inf; rows with a NaN slot lse get NaN.
 template <int D, int R, int DCB_WAVES>
 __global__ __launch_bounds__(64 * DCB_WAVES) void k_dec_combine(const float* __restrict__ part_o,
                                                                 const float* __restrict__ part_lse,
@@ -401,6 +401,7 @@ __global__ __launch_bounds__(64 * DCB_WAVES) void k_dec_combine(const float* __r
                                                                 int T, int G, int K) {
   constexpr int CL = D / 64;  // value columns per lane
   __shared__ float red[DCB_WAVES];
+  __shared__ int red_nan[DCB_WAVES];
   __shared__ float acc[DCB_WAVES][D + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bh = blockIdx.x, H = G * R, b = bh / H, h = bh % H, g = h / R, hh = h % R;
@@ -411,16 +412,28 @@ __global__ __launch_bounds__(64 * DCB_WAVES) void k_dec_combine(const float* __r
   const float* pl = part_lse + (size_t)bg * K * R + hh;
   const float* po = part_o + ((size_t)bg * K * R + hh) * D + CL * lane;
   float M = -INFINITY;
+  bool nan_seen = false;  // a NaN slot lse (skipped by the max) makes the row NaN
   for (int sl = threadIdx.x; sl < K; sl += 64 * DCB_WAVES) {
     const int blk = row[sl];
-    if (blk >= 0 && blk < nb) M = fmaxf(M, pl[(size_t)sl * R]);
+    if (blk >= 0 && blk < nb) {
+      const float x = pl[(size_t)sl * R];
+      M = fmaxf(M, x);
+      nan_seen |= x != x;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[wave] = M;
+  nan_seen = __any(nan_seen);
+  if (lane == 0) {
+    red[wave] = M;
+    red_nan[wave] = nan_seen;
+  }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < DCB_WAVES; ++w) M = fmaxf(M, red[w]);
+  for (int w = 0; w < DCB_WAVES; ++w) {
+    M = fmaxf(M, red[w]);
+    nan_seen |= red_nan[w] != 0;
+  }
   float sw = 0.f, so[CL];
 #pragma unroll
   for (int c = 0; c < CL; ++c) so[c] = 0.f;
@@ -450,9 +463,9 @@ __global__ __launch_bounds__(64 * DCB_WAVES) void k_dec_combine(const float* __r
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < DCB_WAVES; ++w) v += acc[w][CL * lane + c];
-    o[oh * D + CL * lane + c] = f2bf(M == -INFINITY ? 0.f : v / tw);
+    o[oh * D + CL * lane + c] = f2bf(nan_seen ? __builtin_nanf("") : M == -INFINITY ? 0.f : v / tw);
   }
-  if (lane == 0) lse[oh] = M == -INFINITY ? -INFINITY : M + __logf(tw);
+  if (lane == 0) lse[oh] = nan_seen ? __builtin_nanf("") : M == -INFINITY ? -INFINITY : M + __logf(tw);
 }
 
 // ---- host launchers

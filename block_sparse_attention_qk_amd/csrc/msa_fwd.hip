@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
 // group, token) row per R*D/8 threads (each thread owns 8 head-dim values of
 // one head and streams 16 bytes per slot).  A slot holds a partial iff its
 // cache entry is a valid causal block.  A row with no valid entry gets
-// O = 0, LSE = -inf.  WITH_D (the merged forward/backward call) also forms the
+// O = 0, LSE = -inf; a row with a NaN partial (NaN inputs) gets NaN.  WITH_D (the merged forward/backward call) also forms the
 // backward's D = rowsum(dout * O) here, while O is still in registers.
 template <int D, int R, bool WITH_D>
 __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__ idx, const bf16raw* __restrict__ part_o,
@@ -241,6 +241,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
   // branch), and the accumulator is rescaled when the maximum grows.
   constexpr int SB = 16;  // slots per batch: independent loads in flight per thread
   float M = -INFINITY, L = 0.f, acc[8];
+  bool nan_seen = false;  // a NaN partial lse (the running max would skip it) makes the row NaN
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < K; s0 += SB) {
@@ -266,7 +267,10 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
     }
     float mb = M;
 #pragma unroll
-    for (int u = 0; u < SB; ++u) mb = fmaxf(mb, lv[u]);
+    for (int u = 0; u < SB; ++u) {
+      mb = fmaxf(mb, lv[u]);
+      nan_seen |= lv[u] != lv[u];
+    }
     if (mb == -INFINITY) continue;  // no valid slot yet
     const float mbl = mb * LOG2E;
     const float c = fast_exp2(M * LOG2E - mbl);  // 0 while M is still -inf
@@ -286,11 +290,11 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
     }
     M = mb;
   }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const float inv = nan_seen ? __builtin_nanf("") : L > 0.f ? 1.0f / L : 0.f;
   const uint4 ob = make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
                               pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv));
   st16u(o + orow * D + c8, ob);
-  if (c8 == 0) lse[orow] = L > 0.f ? M + fast_log2(L) * LN2 : -INFINITY;
+  if (c8 == 0) lse[orow] = nan_seen ? __builtin_nanf("") : L > 0.f ? M + fast_log2(L) * LN2 : -INFINITY;
   if constexpr (WITH_D) {
     // D = rowsum(dout * o) of the bf16 o just written, summed in the order of
     // k_bwd_dot (8 products per lane, then xor shuffles over the D/8 lanes of
