@@ -9,16 +9,20 @@ timed steps between two device synchronisations.
 
 Printed: one JSON line.  `value` is tokens/s of the whole step on the main
 workload (the 128K configuration: B=1, T=131072, 32 query / 4 KV heads, head
-dim 128, 4 proxy heads of dim 64, top-k 32).  Extra fields give the fwd+bwd
-rate with cached indices, effective TFLOP/s on the executed sparse FLOPs,
-per-phase and per-kernel times (HIP events recorded by the library on the
-launch stream), the roofline of the dominant kernel, extra workloads (the 1M
-configuration; the 128K step on a fixed window/dilation pattern united with
-the proxy top-k; the 128K step through the merged forward/backward call;
-decode steps of 16 sequences at 128K cached tokens), and the
-CPU oracle timed on a bounded sample.
+dim 128, 4 proxy heads of dim 64, top-k 32), from the median of the K
+per-step times (HIP events around each step; the mean is reported beside it).
+Extra fields give the fwd+bwd rate with cached indices, effective TFLOP/s on
+the executed sparse FLOPs, per-phase and per-kernel times (HIP events recorded
+by the library on the launch stream), the roofline of the dominant kernel,
+extra workloads (the 512K and 1M configurations; the 128K step on a fixed
+window/dilation pattern united with the proxy top-k; the 128K step through the
+merged forward/backward call; decode steps of 16 sequences at 128K cached
+tokens), the dense context (topk = N through the same kernels, forward and
+backward ratios), the device memory of separate against merged calls, and the
+CPU oracle timed on bounded samples (extrapolated where marked).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--also 1m,pattern,merged,decode|''] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--also 512k,1m,pattern,merged,decode,dense,memory|''] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ import dataclasses
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -247,13 +252,16 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(stop)
-    phase = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(3)]
     kern = msa.timing_read()
     msa.timing_enable(False)
 
+    # per-step times from the step's own events; the reported figures are medians
+    per_step = [e[0].elapsed_time(e[3]) for e in evs]
+    per_phase = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(3)]
     tokens = cfg.B * cfg.T
-    ms_step = total_ms / steps
-    t_sel, t_fwd, t_bwd = (p / steps for p in phase)
+    ms_step = statistics.median(per_step)
+    t_sel, t_fwd, t_bwd = (statistics.median(p) for p in per_phase)
+    t_fb = statistics.median([a + b for a, b in zip(per_phase[1], per_phase[2])])
     f_pair = 4 * cfg.d * cfg.R * 128  # forward flop per (token, group, block); backward is 2.5x
     f_fwd, f_bwd, f_proxy = f_pair * pairs, 2.5 * f_pair * pairs, cfg.flops_proxy()
     res = {
@@ -261,13 +269,17 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
                     (" merged fwd+bwd (msa_fwd_bwd)" if merged else ""),
         "shape": {"B": cfg.B, "T": cfg.T, "H": cfg.H, "G": cfg.G, "d": cfg.d, "dp": cfg.dp, "topk": cfg.topk,
                   "cache_width": width},
+        "steps": steps,
         "ms_per_step": ms_step,
+        "ms_per_step_mean": total_ms / steps,
+        "ms_per_step_min_max": [min(per_step), max(per_step)],
         "wall_ms_per_step": 1e3 * wall / steps,
         "tokens_per_s": tokens / (ms_step / 1e3),
         "phases_ms": {"select": t_sel, "fwd": t_fwd, "bwd": t_bwd} if not merged else {"select": t_sel,
-                                                                                          "fwd_bwd": t_fwd + t_bwd},
-        "fwd_bwd_tokens_per_s": tokens / ((t_fwd + t_bwd) / 1e3),
-        "fwd_bwd_effective_tflops": (f_fwd + f_bwd) / ((t_fwd + t_bwd) / 1e3) / 1e12,
+                                                                                          "fwd_bwd": t_fb},
+        "fwd_bwd_ms": t_fb,
+        "fwd_bwd_tokens_per_s": tokens / (t_fb / 1e3),
+        "fwd_bwd_effective_tflops": (f_fwd + f_bwd) / (t_fb / 1e3) / 1e12,
         "select_tflops": f_proxy / (t_sel / 1e3) / 1e12,
         "pairs": pairs,
         "flops": {"fwd": f_fwd, "bwd": f_bwd, "proxy": f_proxy},
@@ -282,6 +294,53 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
 
 
 DECODE_BATCH = 16  # sequences per decode step, each at the workload's full context
+
+# timed steps (after one warm-up) of the long-context legs
+LEG_STEPS = {"512k": 5, "1m": 3}
+
+
+def memory_footprint(cfg: synth.Config) -> dict:
+    """Device memory of the Main Branch calls, separate (msa_fwd, then msa_bwd)
+    against merged (msa_fwd_bwd), with cached indices: the activations a
+    training step keeps between forward and backward, and the peak allocated
+    during the calls (workspace, activations and outputs; the inputs q, k, v,
+    dout and idx are resident beforehand and not counted)."""
+    x = gpu_inputs(cfg)
+    idx = msa.msa_proxy_select(x["qp"], x["kp"], cfg.topk)
+    del x["qp"], x["kp"]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    dims = (cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    out = {"workload": cfg.name, "unit": "bytes"}
+    for tag in ("separate", "merged"):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        if tag == "separate":
+            ws = msa.Workspace(nbytes=msa.msa_workspace_bytes(*dims, msa.OP_FWD))
+            o, lse = msa.msa_fwd(x["q"], x["k"], x["v"], idx, ws=ws)
+            ws_f = ws.get(0).numel()
+            del ws
+            kept = o.numel() * o.element_size() + lse.numel() * lse.element_size()
+            ws = msa.Workspace(nbytes=msa.msa_workspace_bytes(*dims, msa.OP_BWD))
+            grads = msa.msa_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, idx, ws=ws)
+            ws_b = ws.get(0).numel()
+            out[tag] = {"workspace_fwd": ws_f, "workspace_bwd": ws_b, "activations_kept": kept}
+        else:
+            ws = msa.Workspace(nbytes=msa.msa_workspace_bytes(*dims, msa.OP_FWD_BWD))
+            res = msa.msa_fwd_bwd(x["q"], x["k"], x["v"], x["dout"], idx, ws=ws)
+            out[tag] = {"workspace": ws.get(0).numel(), "activations_kept": 0}
+            o, lse, grads = res[0], res[1], res[2:]
+        torch.cuda.synchronize()
+        out[tag]["peak_during_calls"] = torch.cuda.max_memory_allocated() - base
+        del ws, o, lse, grads
+    out["activations_kept_note"] = ("between forward and backward the separate calls keep o and lse (idx is kept "
+                                    "by both); the merged call recomputes the forward and keeps nothing more")
+    del x, idx
+    torch.cuda.empty_cache()
+    return out
+
 
 
 def run_dense_context(steps: int) -> dict:
@@ -298,14 +357,17 @@ def run_dense_context(steps: int) -> dict:
         row = {"T": sparse.T}
         for tag, c in (("sparse", sparse), ("dense", dense)):
             r = run_workload(c, steps, 1, host_inputs=False)
-            ms = r["phases_ms"]["fwd"] + r["phases_ms"]["bwd"]
-            row[tag] = {"topk": c.topk, "pairs": r["pairs"], "fwd_bwd_ms": ms,
+            row[tag] = {"topk": c.topk, "pairs": r["pairs"], "fwd_ms": r["phases_ms"]["fwd"],
+                        "bwd_ms": r["phases_ms"]["bwd"], "fwd_bwd_ms": r["fwd_bwd_ms"],
                         "fwd_bwd_effective_tflops": r["fwd_bwd_effective_tflops"],
                         "kernels_ms_per_step": {k: v for k, v in r["kernels_ms_per_step"].items() if v}}
         row["dense_over_sparse_time"] = row["dense"]["fwd_bwd_ms"] / row["sparse"]["fwd_bwd_ms"]
+        row["dense_over_sparse_fwd"] = row["dense"]["fwd_ms"] / row["sparse"]["fwd_ms"]
+        row["dense_over_sparse_bwd"] = row["dense"]["bwd_ms"] / row["sparse"]["bwd_ms"]
         out["runs"].append(row)
-        print("bench: dense context %s: sparse %.1f ms, dense %.1f ms" % (
-            name, row["sparse"]["fwd_bwd_ms"], row["dense"]["fwd_bwd_ms"]), file=sys.stderr, flush=True)
+        print("bench: dense context %s: sparse %.1f ms, dense %.1f ms (fwd %.1fx, bwd %.1fx)" % (
+            name, row["sparse"]["fwd_bwd_ms"], row["dense"]["fwd_bwd_ms"], row["dense_over_sparse_fwd"],
+            row["dense_over_sparse_bwd"]), file=sys.stderr, flush=True)
     return out
 
 
@@ -393,46 +455,154 @@ def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int) -> dict:
             "work_per_launch": work}
 
 
-def cpu_baseline(cfg: synth.Config, target_s: float = 15.0) -> dict:
-    """The oracle, as it stands, on a uniform sample of query tokens of the same
-    workload: Index Branch rows, forward rows and backward dQ rows."""
+def _cpu_host_rows(cfg: synth.Config, rows):
+    """Float64 host inputs for the oracle on the given token rows (B = 1):
+    q, dout and qp hold only those rows (the rest stay untouched zero pages),
+    k, v and kp are whole.  Drawn with synth's seeded per-chunk generators, so
+    the values are the workload's own."""
     import numpy as np
+    assert cfg.B == 1
+    T = cfg.T
+    out = {}
+    for name in ("k", "v", "kp"):
+        parts = [synth.make_tensor(name, cfg, t0, min(T, t0 + (1 << 17))).double().numpy()
+                 for t0 in range(0, T, 1 << 17)]
+        out[name] = np.concatenate(parts, axis=1)
+    for name in ("q", "dout", "qp"):
+        width = (cfg.H, cfg.d) if name != "qp" else (cfg.G, cfg.dp)
+        a = np.zeros((1, T) + width, dtype=np.float64)
+        for c in np.unique(rows // synth.CHUNK):
+            t0, t1 = int(c) * synth.CHUNK, min(T, (int(c) + 1) * synth.CHUNK)
+            sel = rows[(rows >= t0) & (rows < t1)]
+            a[0, sel] = synth.make_tensor(name, cfg, t0, t1).double().numpy()[0, sel - t0]
+        out[name] = a
+    return out
+
+
+def _oracle_rows(cfg, dm, x, rows):
+    """Oracle Index Branch, forward and backward dQ on the sampled rows; seconds of each."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    sel = oracle.select(dm, x["qp"], x["kp"], rows=rows)
+    t1 = time.perf_counter()
+    idx = np.full((cfg.B, cfg.G, cfg.T, cfg.topk), -1, dtype=np.int32)
+    idx[rows // cfg.T, :, rows % cfg.T, :] = sel
+    oracle.fwd(dm, x["q"], x["k"], x["v"], idx, rows=rows)
+    t2 = time.perf_counter()
+    oracle.bwd_rows(dm, x["q"], x["k"], x["v"], x["dout"], idx, rows=rows)
+    t3 = time.perf_counter()
+    return t1 - t0, t2 - t1, t3 - t2
+
+
+def _dkdv_ratio(cfg: synth.Config) -> float:
+    """Cost of the oracle's dK/dV pass relative to its dQ rows on one small
+    full problem with the workload's head shape (T = 2048, one group): the
+    full backward is the dQ rows plus that pass, which repeats each row's score
+    work and scatters into the key rows."""
+    import oracle
+    c = synth.custom(1, 2048, cfg.R, 1, cfg.d, cfg.dp, min(cfg.topk, 16))
+    x = {n: t.double().numpy() for n, t in synth.make_inputs(c, seed_offset=5).items()}
+    dm = oracle.Dims(c.B, c.T, c.H, c.G, c.d, c.dp, c.topk)
+    idx = oracle.select(dm, x["qp"], x["kp"])
+    oracle.bwd_rows(dm, x["q"], x["k"], x["v"], x["dout"], idx)  # warm-up: threads, pages
+    oracle.bwd(dm, x["q"], x["k"], x["v"], x["dout"], idx)
+    t_rows, t_full = [], []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.bwd_rows(dm, x["q"], x["k"], x["v"], x["dout"], idx)
+        t1 = time.perf_counter()
+        oracle.bwd(dm, x["q"], x["k"], x["v"], x["dout"], idx)
+        t2 = time.perf_counter()
+        t_rows.append(t1 - t0)
+        t_full.append(t2 - t1)
+    tr, tf = statistics.median(t_rows), statistics.median(t_full)
+    return max(0.0, tf - tr) / tr
+
+
+def cpu_full(cfg: synth.Config) -> dict:
+    """The whole oracle on the whole workload: Index Branch, forward and the
+    full backward (dQ rows and the dK/dV pass)."""
+    import oracle
+    x = {n: t.double().numpy() for n, t in synth.make_inputs(cfg).items()}
+    dm = oracle.Dims(cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    t0 = time.perf_counter()
+    idx = oracle.select(dm, x["qp"], x["kp"])
+    t1 = time.perf_counter()
+    oracle.fwd(dm, x["q"], x["k"], x["v"], idx)
+    oracle.bwd(dm, x["q"], x["k"], x["v"], x["dout"], idx)
+    t2 = time.perf_counter()
+    tokens = cfg.B * cfg.T
+    return {"config": cfg.name, "value": tokens / (t2 - t0), "unit": "tokens/s", "seconds": t2 - t0,
+            "fwd_bwd_tokens_per_s": tokens / (t2 - t1), "extrapolated": False,
+            "sample": "the whole %s workload: select, fwd and the full bwd; %.1f s" % (cfg.name, t2 - t0)}
+
+
+def cpu_sampled(cfg: synth.Config, n_rows: int, ratio: float, max_chunks: int = 32, seed: int = 1) -> dict:
+    """The oracle on a seeded uniform sample of query tokens of the workload
+    (rows drawn uniformly inside up to `max_chunks` randomly chosen 4096-token
+    chunks), extrapolated to the whole step: the Index Branch by the ratio of
+    causal keys scored, the forward and backward by the ratio of (token, group,
+    block) pairs, the dK/dV pass as `ratio` times the dQ rows' time."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    nchunk = (cfg.T + synth.CHUNK - 1) // synth.CHUNK
+    chunks = np.sort(rng.choice(nchunk, size=min(nchunk, max_chunks), replace=False))
+    per = max(1, n_rows // len(chunks))
+    rows = np.unique(np.concatenate([c * synth.CHUNK + rng.choice(synth.CHUNK, size=per, replace=False)
+                                     for c in chunks]))
+    x = _cpu_host_rows(cfg, rows)
+    dm = oracle.Dims(cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
+    t_sel, t_fwd, t_dq = _oracle_rows(cfg, dm, x, rows)
+    keys_all = cfg.B * cfg.G * cfg.T * (cfg.T + 1) / 2.0
+    keys_s = cfg.G * float(np.sum(rows + 1))
+    pairs_s = cfg.G * float(np.sum(np.minimum(cfg.topk, rows // synth.BLOCK + 1)))
+    f_keys, f_pairs = keys_all / keys_s, cfg.pairs() / pairs_s
+    t_sel_all = t_sel * f_keys
+    t_fb_all = (t_fwd + t_dq * (1.0 + ratio)) * f_pairs
+    tokens = cfg.B * cfg.T
+    return {"config": cfg.name, "value": tokens / (t_sel_all + t_fb_all), "unit": "tokens/s",
+            "fwd_bwd_tokens_per_s": tokens / t_fb_all, "seconds_sampled": t_sel + t_fwd + t_dq,
+            "seconds_extrapolated": t_sel_all + t_fb_all, "extrapolated": True,
+            "sample": ("%d query tokens from %d of %d chunks of the %s workload; select, fwd and dQ rows timed "
+                       "(%.1f s), extrapolated by causal keys scored (x%.0f) and by pairs (x%.0f); the dK/dV "
+                       "pass counted as %.2fx the dQ rows" % (len(rows), len(chunks), nchunk, cfg.name,
+                                                               t_sel + t_fwd + t_dq, f_keys, f_pairs, ratio))}
+
+
+def cpu_baseline(cfg: synth.Config, target_s: float = 15.0, others=("tiny", "16k", "512k", "1m")) -> dict:
+    """The oracle as it stands, timed on this host's cores: the main workload
+    on a sample of about target_s seconds extrapolated to the whole step, a
+    single-thread rate on a smaller sample, and one entry per other
+    configuration (tiny and 16K whole, 512K and 1M sampled and extrapolated)."""
     import oracle
 
     oracle.build()
     cores = len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
-    x = synth.make_inputs(cfg)
-    f64 = {n: x[n].double().numpy() for n in x}
-    dm = oracle.Dims(cfg.B, cfg.T, cfg.H, cfg.G, cfg.d, cfg.dp, cfg.topk)
-    rng = np.random.default_rng(1)
-
-    def run(n_rows):
-        rows = np.sort(rng.choice(cfg.B * cfg.T, size=n_rows, replace=False))
-        t0 = time.perf_counter()
-        sel = oracle.select(dm, f64["qp"], f64["kp"], rows=rows)                 # [n, G, k]
-        idx = np.full((cfg.B, cfg.G, cfg.T, cfg.topk), -1, dtype=np.int32)
-        b_, t_ = rows // cfg.T, rows % cfg.T
-        idx[b_, :, t_, :] = sel
-        oracle.fwd(dm, f64["q"], f64["k"], f64["v"], idx, rows=rows)
-        oracle.bwd_rows(dm, f64["q"], f64["k"], f64["v"], f64["dout"], idx, rows=rows)
-        return time.perf_counter() - t0
-
-    pilot_rows = 16
-    t_pilot = run(pilot_rows)
-    n = int(min(4096, max(pilot_rows, pilot_rows * target_s / max(t_pilot, 1e-3))))
-    t = run(n)
-    # the same kind of sample on one thread, about a third of the time budget
+    ratio = _dkdv_ratio(cfg)
+    pilot = cpu_sampled(cfg, 64, ratio)
+    n = int(min(4096, max(64, 64 * target_s / max(pilot["seconds_sampled"], 1e-3))))
+    main = cpu_sampled(cfg, n, ratio, seed=2)
     oracle.set_threads(1)
-    n1 = int(max(8, min(n, (n / t) / cores * (target_s / 3))))
-    t1 = run(n1)
+    n1 = int(max(16, min(n, n / main["seconds_sampled"] / cores * (target_s / 3))))
+    single = cpu_sampled(cfg, n1, ratio, seed=3)
     oracle.set_threads(cores)
-    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": ("%d query tokens drawn uniformly from the %s workload: Index Branch rows, forward rows and "
-                       "backward dQ rows over all heads and groups (the oracle's dK/dV pass is not in the sample); "
-                       "%.1f s on %d threads" % (n, cfg.name, t, cores)),
-            "single_thread": {"value": n1 / t1, "unit": "tokens/s", "cores": 1,
-                              "sample": "%d query tokens of the same kind; %.1f s on 1 thread" % (n1, t1)}}
+    per_config = []
+    for name in others:
+        c = synth.CONFIGS[name]
+        print("bench: cpu baseline %s" % name, file=sys.stderr, flush=True)
+        if c.T <= 16384:
+            per_config.append(cpu_full(c))
+        else:
+            per_config.append(cpu_sampled(c, 32 if c.topk > 128 else 64, _dkdv_ratio(c), max_chunks=8, seed=4))
+    return {"value": main["value"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": main["sample"] + "; %d threads" % cores, "extrapolated": True,
+            "fwd_bwd_tokens_per_s": main["fwd_bwd_tokens_per_s"],
+            "single_thread": {"value": single["value"], "unit": "tokens/s", "cores": 1,
+                              "sample": single["sample"] + "; 1 thread"},
+            "per_config": per_config}
 
 
 def main() -> int:
@@ -441,13 +611,14 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="128k", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--also", default="1m,pattern,merged,decode,dense",
+    ap.add_argument("--also", default="512k,1m,pattern,merged,decode,dense,memory",
                     help="comma list of extra workloads: config names, 'pattern' (the main config with the fixed "
                          "window/dilation pattern united with the proxy top-k), 'merged' (the main config through "
                          "msa_fwd_bwd), 'decode' (decode steps of %d sequences at the main config's full context), "
-                         "'dense' (16K and 128K at topk = N beside their sparse configurations); '' for none"
-                         % DECODE_BATCH)
-    ap.add_argument("--also-steps", type=int, default=2)
+                         "'dense' (16K and 128K at topk = N beside their sparse configurations), 'memory' (device "
+                         "memory of separate against merged calls at 128K and 1M); '' for none" % DECODE_BATCH)
+    ap.add_argument("--also-steps", type=int, default=0,
+                    help="timed steps of the config legs (0: 5 at 512K, 3 at 1M) and of the dense context (0: 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference kernel for traffic counters)")
@@ -489,6 +660,7 @@ def main() -> int:
     print("bench: main workload done: %.3f ms/step" % main_res["ms_per_step"], file=sys.stderr, flush=True)
     extra = []
     dense_context = None
+    memory = None
     for name in [s for s in args.also.split(",") if s and s != args.config]:
         if name == "pattern":
             print("bench: extra workload %s + pattern %s" % (cfg, PATTERN), file=sys.stderr, flush=True)
@@ -502,7 +674,11 @@ def main() -> int:
             continue
         if name == "dense":
             print("bench: dense context (topk = N) at 16K and 128K", file=sys.stderr, flush=True)
-            dense_context = run_dense_context(args.also_steps)
+            dense_context = run_dense_context(args.also_steps or 2)
+            continue
+        if name == "memory":
+            print("bench: device memory, separate against merged calls", file=sys.stderr, flush=True)
+            memory = [memory_footprint(synth.CONFIGS[c]) for c in ("128k", "1m")]
             continue
         if name == "decode":
             print("bench: decode steps, %d sequences of %s" % (DECODE_BATCH, cfg), file=sys.stderr, flush=True)
@@ -511,7 +687,7 @@ def main() -> int:
             continue
         c = synth.CONFIGS[name]
         print("bench: extra workload %s" % (c,), file=sys.stderr, flush=True)
-        extra.append(run_workload(c, args.also_steps, 1, host_inputs=False))
+        extra.append(run_workload(c, args.also_steps or LEG_STEPS.get(name, 3), 1, host_inputs=False))
         print("bench: %s done: %.1f ms/step" % (name, extra[-1]["ms_per_step"]), file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
@@ -545,6 +721,8 @@ def main() -> int:
     }
     if dense_context is not None:
         line["dense_context"] = dense_context
+    if memory is not None:
+        line["memory"] = memory
     print(json.dumps(line))
     return 0
 
