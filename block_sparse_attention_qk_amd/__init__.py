@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
   msa_pattern_select(B, T, G, window, dilation, idx_in) -> idx   (fixed block pattern)
   msa_decode_select(qp, kp, lens, topk)        -> idx            (decode step, Index Branch)
   msa_decode_fwd(q, k, v, lens, idx, scale)    -> (o, lse)       (decode step, Main Branch)
+  msa_decode_fwd_static(q, k, v, lens, idx)    -> (o, lse)       (the same without a workspace)
 Layouts: qp, kp [B,T,G,dp] bf16; q, o, dout [B,T,H,d] bf16; k, v [B,T,G,d] bf16;
 idx [B,G,T,topk] int32; lse [B,T,H] fp32.  Decode: qp [B,G,dp], q and o [B,H,d],
 caches kp/k/v [B,T,G,*], lens [B] int32 (on the device), idx [B,G,topk], lse [B,H].
@@ -31,7 +32,7 @@ import torch
 __all__ = [
     "MsaError", "Workspace", "lib_path", "load", "msa_workspace_bytes", "msa_workspace_min_bytes",
     "msa_proxy_select", "msa_pattern_select", "pattern_width", "msa_fwd", "msa_bwd", "msa_fwd_bwd",
-    "msa_decode_select", "msa_decode_fwd", "OP_SELECT", "OP_FWD", "OP_BWD", "OP_DECODE_SELECT", "OP_DECODE_FWD",
+    "msa_decode_select", "msa_decode_fwd", "msa_decode_fwd_static", "STATIC_SCRATCH_BYTES", "OP_SELECT", "OP_FWD", "OP_BWD", "OP_DECODE_SELECT", "OP_DECODE_FWD",
     "OP_FWD_BWD", "EXPORTED_SYMBOLS",
     "KERNEL_NAMES", "timing_enable", "timing_read",
 ]
@@ -43,7 +44,8 @@ _lib = None
 OP_SELECT, OP_FWD, OP_BWD, OP_DECODE_SELECT, OP_DECODE_FWD, OP_FWD_BWD = 0, 1, 2, 3, 4, 5
 EXPORTED_SYMBOLS = ("msa_workspace_bytes", "msa_workspace_min_bytes", "msa_proxy_select", "msa_pattern_select",
                     "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select", "msa_decode_fwd",
-                    "msa_status_str", "msa_version", "msa_timing_enable", "msa_timing_read")
+                    "msa_decode_fwd_static", "msa_status_str", "msa_version", "msa_timing_enable", "msa_timing_read")
+STATIC_SCRATCH_BYTES = 16 << 20  # MSA_STATIC_SCRATCH_BYTES (include/msa.h)
 
 # msa_kernel_id values (include/msa.h)
 KERNEL_NAMES = ("proxy_pool", "topk", "inverse", "fwd_partials", "fwd_combine", "bwd_dot", "bwd_partials",
@@ -84,8 +86,9 @@ def load():
     lib.msa_fwd_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_decode_select.argtypes = [D, P, P, P, P, P, SZ, P]
     lib.msa_decode_fwd.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_decode_fwd_static.argtypes = [D, P, P, P, P, P, P, P, P]
     for f in ("msa_proxy_select", "msa_pattern_select", "msa_fwd", "msa_bwd", "msa_fwd_bwd", "msa_decode_select",
-              "msa_decode_fwd"):
+              "msa_decode_fwd", "msa_decode_fwd_static"):
         getattr(lib, f).restype = I
     lib.msa_status_str.argtypes = [I]
     lib.msa_status_str.restype = ctypes.c_char_p
@@ -416,3 +419,15 @@ def msa_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torc
                                  _ptr(lse), _ptr(w), w.numel(), _stream(q.device)))
     return o, lse
 
+
+def msa_decode_fwd_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor,
+                          idx: torch.Tensor, scale: float = 0.0,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """msa_decode_fwd without a workspace: the library's static device scratch
+    holds the partials (include/msa.h, msa_decode_fwd_static).  With `out`
+    given, nothing is allocated on the device; calls on one GPU share the
+    scratch and must not overlap."""
+    dims, _, o, lse = _decode_fwd_args(q, k, v, lens, idx, scale, out)
+    _check(load().msa_decode_fwd_static(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(idx),
+                                        _ptr(o), _ptr(lse), _stream(q.device)))
+    return o, lse

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "msa.h"
@@ -214,6 +215,34 @@ int timing_begin(int kernel, hipStream_t st) {
 
 void timing_end(int id, hipStream_t st) {
   if (id >= 0) (void)hipEventRecord(t_timing->slot[id].b, st);
+}
+
+// ---- allocation-free decode attention (msa_decode_fwd_static)
+// Its per-slot partials live in this array instead of a caller workspace.
+// In host code `scratch` names a host-side stand-in; the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current and kept here.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)MSA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the device that `st` belongs to, which must
+// be the current device.
+msa_status scratch_for_stream(hipStream_t st, void** out) {
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_HIP;
+  if (hipStreamGetDevice(st, &sdev) != hipSuccess) return MSA_ERR_HIP;
+  if (dev != sdev || dev < 0 || dev >= MAX_DEVICES) return MSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MSA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MSA_OK;
 }
 
 // Launch `call` (a hipError_t expression), timed as `kernel` when timing is on.
@@ -466,6 +495,26 @@ msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf1
   return MSA_OK;
 }
 
+msa_status msa_decode_fwd_static(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                                 const int32_t* len, const int32_t* idx, msa_bf16* o, float* lse, void* stream) {
+  Geo g;
+  const msa_status s = make_dec_geo(dims, MSA_OP_DECODE_FWD, &g);
+  if (s != MSA_OK) return s;
+  if (!q || !k || !v || !len || !idx || !o || !lse) return MSA_ERR_NULL;
+  if (!al16(q) || !al16(k) || !al16(v) || !al16(len) || !al16(idx) || !al16(o) || !al16(lse)) return MSA_ERR_ALIGN;
+  const Layout L = layout(g, MSA_OP_DECODE_FWD, 0);
+  if (L.total > STATIC_SCRATCH_BYTES) return MSA_ERR_SCRATCH;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* base = nullptr;
+  if (const msa_status e = scratch_for_stream(st, &base); e != MSA_OK) return e;
+  char* b = static_cast<char*>(base);
+  float* part_o = reinterpret_cast<float*>(b + L.part_o);
+  float* part_lse = reinterpret_cast<float*>(b + L.part_lse);
+  MSA_LAUNCH(MSA_K_DEC_ATTN, st, launch_dec_attn(g, q, k, v, len, idx, part_o, part_lse, st));
+  MSA_LAUNCH(MSA_K_DEC_COMBINE, st, launch_dec_combine(g, part_o, part_lse, idx, len, o, lse, st));
+  return MSA_OK;
+}
+
 const char* msa_status_str(msa_status s) {
   switch (enum_value(s)) {
     case MSA_OK: return "ok";
@@ -476,6 +525,7 @@ const char* msa_status_str(msa_status s) {
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_HIP: return "HIP runtime error";
     case MSA_ERR_INDEX: return "block-index cache fails the MSA_VALIDATE check";
+    case MSA_ERR_SCRATCH: return "problem needs more than the library's static scratch (MSA_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -83,7 +83,8 @@ typedef enum {
   MSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   MSA_ERR_WORKSPACE = 5,   /* ws_bytes below msa_workspace_min_bytes */
   MSA_ERR_HIP = 6,         /* the HIP runtime reported an error */
-  MSA_ERR_INDEX = 7        /* MSA_VALIDATE set: idx is not a valid cache (nothing else ran) */
+  MSA_ERR_INDEX = 7,       /* MSA_VALIDATE set: idx is not a valid cache (nothing else ran) */
+  MSA_ERR_SCRATCH = 8      /* msa_decode_fwd_static: the problem needs more than MSA_STATIC_SCRATCH_BYTES */
 } msa_status;
 
 typedef struct {
@@ -219,6 +220,26 @@ msa_status msa_decode_select(const msa_dims* dims, const msa_bf16* qp, const msa
 msa_status msa_decode_fwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
                           const int32_t* len, const int32_t* idx, msa_bf16* o, float* lse, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* ---- Decode attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).
+ *
+ * Same arguments, layouts, results and errors as msa_decode_fwd, minus ws and
+ * ws_bytes: the per-slot partials live in a static device array of
+ * MSA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing.  It returns
+ * MSA_ERR_SCRATCH, with nothing enqueued, when the problem needs more than
+ * that, i.e. when msa_workspace_bytes(dims, MSA_OP_DECODE_FWD) exceeds
+ * MSA_STATIC_SCRATCH_BYTES (16 sequences x 4 groups x top-32 x 8 heads x
+ * d 128 need 8.1 MiB).  It runs on the current device, and stream must belong
+ * to it (MSA_ERR_UNSUPPORTED otherwise).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  No part of the array needs
+ * to start at zero: each call writes every partial it reads. */
+#define MSA_STATIC_SCRATCH_BYTES (16u << 20)
+msa_status msa_decode_fwd_static(const msa_dims* dims, const msa_bf16* q, const msa_bf16* k, const msa_bf16* v,
+                                 const int32_t* len, const int32_t* idx, msa_bf16* o, float* lse, void* stream);
 
 /* ---- Optional launch timing, for benchmarks and profiling tools.
  * When enabled, the library records a pair of HIP events on the call's stream

@@ -67,7 +67,10 @@ int main() {
   EXPECT(msa_pattern_select(&d, 8, 64, nullptr, 0, i(P), nullptr), MSA_ERR_SHAPE);  // rows wider than topk 4
   EXPECT(msa_decode_select(&d, b(P), b(P), i(P), i(P), P, 0, nullptr), MSA_ERR_WORKSPACE);
   EXPECT(msa_decode_fwd(&d, b(P), b(P), b(P), i(P), i(P), b(P), f(P), nullptr, 0, nullptr), MSA_ERR_NULL);
-  for (int s = MSA_OK; s <= MSA_ERR_INDEX; ++s)
+  EXPECT(msa_decode_fwd_static(&d, b(P), b(P), b(Q), i(P), i(P), b(P), f(P), nullptr), MSA_ERR_ALIGN);
+  msa_dims big = {64, 256, 32, 4, 128, 64, 32, 0.f};
+  EXPECT(msa_decode_fwd_static(&big, b(P), b(P), b(P), i(P), i(P), b(P), f(P), nullptr), MSA_ERR_SCRATCH);
+  for (int s = MSA_OK; s <= MSA_ERR_SCRATCH; ++s)
     if (msa_status_str((msa_status)s) == nullptr) return 1;
   double ms[MSA_K_COUNT];
   int32_t n[MSA_K_COUNT];

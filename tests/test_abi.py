@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib, msa):
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(8):
+    for code in range(9):
         s = lib.msa_status_str(code)
         assert s and s.decode() not in seen
         seen.add(s.decode())
@@ -260,3 +260,24 @@ def test_missing_library_fails_loudly(msa, monkeypatch, tmp_path):
     with pytest.raises(msa.MsaError):
         msa.msa_workspace_bytes(1, 1024, 8, 2, 128, 64, 4, msa.OP_FWD)
 
+
+def test_decode_fwd_static_checks(lib, msa):
+    """Host-side checks of the allocation-free decode call: they return before
+    any HIP call, so they run without a GPU."""
+    P, Q = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    f = lib.msa_decode_fwd_static
+    d = _dims(msa, B=2, T=1024, topk=8)
+    assert f(None, P, P, P, P, P, P, P, None) == ERR_NULL
+    for i in range(7):
+        args = [P] * 7
+        args[i] = None
+        assert f(ctypes.byref(d), *args, None) == ERR_NULL, i
+        args[i] = Q
+        assert f(ctypes.byref(d), *args, None) == ERR_ALIGN, i
+    for kw, code in ((dict(T=1000), ERR_SHAPE), (dict(H=6, G=2), ERR_UNSUP), (dict(d=96), ERR_UNSUP)):
+        assert f(ctypes.byref(_dims(msa, **kw)), P, P, P, P, P, P, P, None) == code, kw
+    # 64 sequences x 4 groups x top-32 x 8 heads x d 128 fp32 partials: 32 MiB > the 16 MiB scratch
+    big = _dims(msa, B=64, T=256, H=32, G=4, d=128, topk=32)
+    assert lib.msa_workspace_bytes(ctypes.byref(big), msa.OP_DECODE_FWD) > msa.STATIC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), P, P, P, P, P, P, P, None) == 8  # MSA_ERR_SCRATCH
+    assert "static scratch" in lib.msa_status_str(8).decode()
