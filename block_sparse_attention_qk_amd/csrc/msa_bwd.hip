@@ -131,14 +131,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     // when the staged registers go to LDS.
     const int srow = tid >> 3, ssub = tid & 7;
     uint4 sq[2][CPT], sdo[2][CPT];
-    int s_li[2] = {len, len}, s_pair[2] = {0, 0};
+    int s_li[2] = {len, len}, s_ent[2] = {0, 0};
     float s_lse[2] = {0.f, 0.f}, s_dd[2] = {0.f, 0.f};
     auto list_entry = [&](int ti) { return lsts[min(ti * TT + srow / R, len - 1)]; };
-    auto stage_load = [&](auto setc, int ti, int pair) {
+    auto stage_load = [&](auto setc, int ti, int ent) {
       constexpr int st = decltype(setc)::value;
       s_li[st] = ti * TT + srow / R;
-      s_pair[st] = pair;
-      const int t = t0 + pair / K;
+      s_ent[st] = ent;
+      const int t = t0 + (ent >> LIST_SLOT_BITS);
       const size_t hrow = (size_t)(b * T + t) * H + g * R + srow % R;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
@@ -159,10 +159,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       // The row's 8 threads hold the same values and all write them: no branch,
       // so the waits for the staging loads stay exact.
       const bool val = s_li[st] < len;  // a row past the list: P = 0 (LSE = +inf), no key allowed, no dQ
+      const int tl = s_ent[st] >> LIST_SLOT_BITS;
       rlse[buf][srow] = val ? s_lse[st] * LOG2E : INFINITY;
       rdd[buf][srow] = s_dd[st] * scale;
-      rlim[buf][srow] = val ? t0 + s_pair[st] / K - blk * BLK : -1;
-      rpair[buf][srow] = val ? s_pair[st] : -1;
+      rlim[buf][srow] = val ? t0 + tl - blk * BLK : -1;
+      rpair[buf][srow] = val ? tl * K + (s_ent[st] & ((1 << LIST_SLOT_BITS) - 1)) : -1;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -183,7 +184,10 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     // buffer and register-set indices are compile-time constants in each copy
     // of the 6-way unrolled loop ((i+1) mod 3, (i+1) mod 2, (i+2) mod 3 and
     // i mod 2, the set that tile i+2 arrived in and tile i+4 loads into).
-    auto produce = [&](auto qbc, auto pbc, auto sbc, auto setc, int i) {
+    // MASK: only a block's first item can hold the block's own tokens, whose
+    // keys past the query are masked; other items skip the per-key compares.
+    auto produce = [&](auto maskc, auto qbc, auto pbc, auto sbc, auto setc, int i) {
+      constexpr bool MASK = decltype(maskc)::value;
       constexpr int qb = decltype(qbc)::value, pb = decltype(pbc)::value, sb = decltype(sbc)::value;
       const int pair4 = list_entry(i + 4);  // for this iteration's staging load
       if (i + 1 < ntiles) {
@@ -202,15 +206,21 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
           const int r0 = 8 * jj + 4 * h;
           const float4 lv = *reinterpret_cast<const float4*>(&rlse[qb][r0]);
           const float4 dv4 = *reinterpret_cast<const float4*>(&rdd[qb][r0]);
-          const int4 lm = *reinterpret_cast<const int4*>(&rlim[qb][r0]);
           const float la[4] = {lv.x, lv.y, lv.z, lv.w}, da[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-          const int ma[4] = {lm.x, lm.y, lm.z, lm.w};
+          int ma[4] = {BLK, BLK, BLK, BLK};
+          if constexpr (MASK) {
+            const int4 lm = *reinterpret_cast<const int4*>(&rlim[qb][r0]);
+            ma[0] = lm.x;
+            ma[1] = lm.y;
+            ma[2] = lm.z;
+            ma[3] = lm.w;
+          }
           float pv[4], dsv[4];
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int e = 4 * jj + ii;
             const float ex = fast_exp2(sacc[e] * sl2 - la[ii]);
-            pv[ii] = kown <= ma[ii] ? ex : 0.f;
+            pv[ii] = !MASK || kown <= ma[ii] ? ex : 0.f;
             dsv[ii] = pv[ii] * fmaf(pacc[e], scale, -da[ii]);
           }
           const int o = kown * TR + 8 * pswz(kown, jj) + 4 * h;
@@ -226,14 +236,20 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     // The six steps run unconditionally (steps past the last tile only stage
     // clamped rows), so the loop body is straight-line code and the waits for
     // the staging loads count exactly; the consumer runs the same steps.
-    for (int i0 = -1; i0 < ntiles; i0 += 6) {
-      produce(I0{}, I0{}, I1{}, I1{}, i0);
-      produce(I1{}, I1{}, I2{}, I0{}, i0 + 1);
-      produce(I2{}, I0{}, I0{}, I1{}, i0 + 2);
-      produce(I0{}, I1{}, I1{}, I0{}, i0 + 3);
-      produce(I1{}, I0{}, I2{}, I1{}, i0 + 4);
-      produce(I2{}, I1{}, I0{}, I0{}, i0 + 5);
-    }
+    auto loop = [&](auto mc) {
+      for (int i0 = -1; i0 < ntiles; i0 += 6) {
+        produce(mc, I0{}, I0{}, I1{}, I1{}, i0);
+        produce(mc, I1{}, I1{}, I2{}, I0{}, i0 + 1);
+        produce(mc, I2{}, I0{}, I0{}, I1{}, i0 + 2);
+        produce(mc, I0{}, I1{}, I1{}, I0{}, i0 + 3);
+        produce(mc, I1{}, I0{}, I2{}, I1{}, i0 + 4);
+        produce(mc, I2{}, I1{}, I0{}, I0{}, i0 + 5);
+      }
+    };
+    if (it.w & ITEM_DIAG)
+      loop(std::true_type{});
+    else
+      loop(std::false_type{});
   } else {
     // =================== consumer ===================
     f32x16 dka[NCT], dva[NCT];
@@ -330,7 +346,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     }
 
     // ---- dK, dV of the owned keys: lane holds head-dim column 32c + l32, keys 32kq + 8j + 4h + i.
-    if (it.w) {  // one of several items of this block: they run concurrently, so add atomically
+    if (it.w & ITEM_SPLIT) {  // one of several items of this block: they run concurrently, so add atomically
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll

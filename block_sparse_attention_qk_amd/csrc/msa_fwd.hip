@@ -14,6 +14,8 @@
 #include "msa_common.h"
 #include "msa_internal.h"
 
+#include <type_traits>
+
 namespace msa {
 
 // Position of 16-byte chunk c of row r in a swizzled row-major tile of DCH
@@ -86,10 +88,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   const int row = 32 * wave + l32;
   const int tt = row / R, hh = row % R;
   auto list_entry = [&](int ti) { return lsts[min(ti * TT + tt, len - 1)]; };
-  auto load_q = [&](int ti, int pair, bf16x8* bq, int& pr, int& lim) {
+  auto load_q = [&](int ti, int ent, bf16x8* bq, int& pr, int& lim) {
     const bool val = ti * TT + tt < len;
-    const int t = t0 + pair / K;
-    pr = val ? pair : -1;
+    const int tl = ent >> LIST_SLOT_BITS, t = t0 + tl;
+    pr = val ? tl * K + (ent & ((1 << LIST_SLOT_BITS) - 1)) : -1;
     lim = val ? t - blk * BLK : BLK - 1;
     const bf16raw* qr = q + ((size_t)(b * T + t) * H + g * R + hh) * D + 8 * h;
 #pragma unroll
@@ -107,6 +109,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bq[ks]));
   __syncthreads();
 
+  // Only a block's first item can hold the block's own tokens, whose rows
+  // need the causal mask inside the block; every other item runs the loop
+  // without the per-key compares.
+  auto tiles = [&](auto maskc) {
+  constexpr bool MASK = decltype(maskc)::value;
   for (int ti = 0; ti < ntiles; ++ti) {
     const int pair1 = list_entry(ti + 1);
     // S^T = K Q^T: 4 key tiles of 32 along M, this wave's 32 rows along N
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3);
-        const float sv = kk > clim ? -INFINITY : acc[kt][e];
+        const float sv = MASK && kk > clim ? -INFINITY : acc[kt][e];
         acc[kt][e] = sv;
         m = fmaxf(m, sv);
       }
@@ -205,6 +212,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
       part_lse[pidx * R + hh] = m * scale + fast_log2(l) * LN2;  // both lane halves hold the same value
     }
   }
+  };
+  if (it.w & ITEM_DIAG)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
 }
 
 // Exact log-sum-exp merge of a token's per-block partials, one (batch,

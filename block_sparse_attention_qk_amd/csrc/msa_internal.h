@@ -24,6 +24,16 @@ constexpr int FWD_ITEM_TOKENS = 256;  // tokens per forward work item (list chun
 // into several items that run in parallel and add their dK/dV atomically.
 constexpr int BWD_ITEM_TOKENS = 4096;
 
+// Pair-list entries hold (t - t0) << LIST_SLOT_BITS | slot: the token offset
+// in the window and the cache slot (topk <= 1024, windows <= 2^20 tokens).
+constexpr int LIST_SLOT_BITS = 10;
+// Work item flags (.w of {block, start, len, flags}).
+constexpr int ITEM_SPLIT = 1;  // the block's list is cut into several items
+constexpr int ITEM_DIAG = 2;   // the block's first item: the only one that can hold the block's own tokens
+// The block's own tokens sit in the first counting-sort chunk of its list, so
+// they all fall into its first item as long as an item holds a whole chunk.
+static_assert(FWD_ITEM_TOKENS >= INV_CHUNK && BWD_ITEM_TOKENS >= INV_CHUNK, "items must hold a whole chunk");
+
 // ---- Index Branch
 hipError_t launch_proxy_pool(const Geo& g, const Win& w, const uint16_t* qp, const uint16_t* kp,
                              float* pooled, hipStream_t st);
@@ -34,9 +44,9 @@ struct InvBufs {
   int32_t* counts;      // [BG][nchunk][N]
   int32_t* base;        // [BG][N]   list start of each block
   int32_t* len;         // [BG][N]   list length of each block
-  int4* items;          // [BG][max_items]  {block, start, len, split}
+  int4* items;          // [BG][max_items]  {block, start, len, ITEM_* flags}
   int32_t* item_count;  // [BG]
-  int32_t* list;        // [BG][W * K]  pair ids (t - t0) * K + slot
+  int32_t* list;        // [BG][W * K]  entries (t - t0) << LIST_SLOT_BITS | slot
   int max_items;
 };
 int inv_max_items(const Geo& g, int W, int item_tokens);

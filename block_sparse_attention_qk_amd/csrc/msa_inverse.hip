@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256) void k_inv_colscan(int32_t* __restrict__ count
 }
 
 // One workgroup per (batch, group): exclusive scan of list lengths -> base,
-// and the work items {block, start, len, split} that cut each list into pieces
-// of at most item_tokens pairs, in block order (split = 1 when a block's list
-// spans several items).
+// and the work items {block, start, len, flags} that cut each list into pieces
+// of at most item_tokens pairs, in block order (flags: ITEM_SPLIT when a
+// block's list spans several items, ITEM_DIAG on a block's first item).
 __global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restrict__ len, int32_t* __restrict__ base,
                                                         int4* __restrict__ items, int32_t* __restrict__ item_count,
                                                         int N, int max_items, int item_tokens) {
@@ -103,13 +103,14 @@ __global__ __launch_bounds__(1024) void k_inv_blockscan(const int32_t* __restric
     if (blk >= N) break;
     const int l = L[blk];
     base[(size_t)bg * N + blk] = run_l;
-    const int split = l > item_tokens ? 1 : 0;  // .w: the block's list is cut into several items
-    for (int s = 0; s < l; s += item_tokens) it[run_i++] = make_int4(blk, run_l + s, min(item_tokens, l - s), split);
+    const int split = l > item_tokens ? ITEM_SPLIT : 0;
+    for (int s = 0; s < l; s += item_tokens)
+      it[run_i++] = make_int4(blk, run_l + s, min(item_tokens, l - s), split | (s == 0 ? ITEM_DIAG : 0));
     run_l += l;
   }
 }
 
-// list[bg][pos] = (t - t0) * K + slot, grouped by block.
+// list[bg][pos] = (t - t0) << LIST_SLOT_BITS | slot, grouped by block.
 __global__ __launch_bounds__(INV_THREADS) void k_inv_scatter(const int32_t* __restrict__ idx,
                                                              const int32_t* __restrict__ counts,
                                                              const int32_t* __restrict__ base,
@@ -134,9 +135,10 @@ __global__ __launch_bounds__(INV_THREADS) void k_inv_scatter(const int32_t* __re
 #pragma unroll
     for (int u = 0; u < INV_UNROLL; ++u) {
       const int e = e0 + u * INV_THREADS;
-      if (blk[u] >= 0 && blk[u] <= (t0 + tl0 + e / K) / BLK) {
+      const int tl = tl0 + e / K;
+      if (blk[u] >= 0 && blk[u] <= (t0 + tl) / BLK) {
         const int pos = atomicAdd(&cur[blk[u]], 1);
-        out[pos] = tl0 * K + e;
+        out[pos] = (tl << LIST_SLOT_BITS) | (e - (tl - tl0) * K);
       }
     }
   }
