@@ -22,7 +22,7 @@ constexpr int FWD_ITEM_TOKENS = 256;  // tokens per forward work item (list chun
 // Backward items hold at most this many pairs: a block picked by more tokens
 // (early blocks, or a fixed pattern's far blocks that every query reads) is cut
 // into several items that run in parallel and add their dK/dV atomically.
-constexpr int BWD_ITEM_TOKENS = 2048;
+constexpr int BWD_ITEM_TOKENS = 1024;
 
 // Pair-list entries hold (t - t0) << LIST_SLOT_BITS | slot: the token offset
 // in the window and the cache slot (topk <= 1024, windows <= 2^20 tokens).

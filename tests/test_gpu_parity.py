@@ -159,7 +159,7 @@ def test_small_workspace_walks_windows(msa):
 # A backward work item holds at most this many pairs; a block selected by more
 # tokens is cut into several items whose dK/dV meet in one accumulator through
 # float atomics.
-BWD_ITEM_PAIRS = 2048
+BWD_ITEM_PAIRS = 1024
 
 
 def _sampled_check(msa, oracle_mod, cfg, n_rows, blocks_per_group, seed=0, split_blocks=()):
