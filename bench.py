@@ -287,7 +287,7 @@ def run_workload(cfg: synth.Config, steps: int, warmup: int, host_inputs: bool, 
         "kernel_launches_per_step": {k: v[1] / steps for k, v in kern.items()},
     }
     res["fwd_bwd_frac_of_peak"] = res["fwd_bwd_effective_tflops"] / PEAK_BF16_TFLOPS
-    res["roofline"] = roofline(cfg, kern, steps, pairs)
+    res["roofline"] = roofline(cfg, kern, steps, pairs, res["workload"])
     del x, ws, idx, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
     return res
@@ -424,9 +424,12 @@ def run_decode(cfg: synth.Config, B: int, steps: int, warmup: int) -> dict:
     return res
 
 
-def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int) -> dict:
+def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int, traffic_key: str = "") -> dict:
     """Roofline entry of the kernel with the largest time: algorithmic work per
-    launch divided by its average launch duration."""
+    launch divided by its average launch duration.  `traffic_key` names the
+    workload whose committed counter summary applies (the plain workload by
+    default); legs with other launch patterns pass their own name, for which no
+    summary exists, so their traffic is reported as unknown."""
     name = max(kern, key=lambda k: kern[k][0])
     ms, launches = kern[name]
     avg_s = ms / max(launches, 1) / 1e3
@@ -451,7 +454,8 @@ def roofline(cfg: synth.Config, kern: dict, steps: int, pairs: int) -> dict:
     else:
         achieved, peak = work / avg_s / 1e9, PEAK_HBM_GBS
     return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": stored_traffic(cfg.name, name), "avg_launch_ms": avg_s * 1e3,
+            "frac": achieved / peak, "traffic": stored_traffic(traffic_key or cfg.name, name),
+            "avg_launch_ms": avg_s * 1e3,
             "work_per_launch": work}
 
 
