@@ -226,11 +226,14 @@ def test_128k_config_sampled(msa, oracle_mod):
                    split_blocks=[(0, 0), (1, 100), (2, 300)])
 
 
-def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
+def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0, split_from_end=()):
     """Full-size run with inputs drawn on the GPU (same recipe as synth: N(0,1)
     bf16, block-mean proxy keys), checked on sampled rows and on late key
-    blocks.  The oracle gets full-size host arrays in which only the rows it
-    reads are filled (the rest stay untouched zero pages)."""
+    blocks.  split_from_end: further blocks (counted from the end) that must be
+    read by more tokens than one backward item holds, so that their dK/dV are
+    added atomically from several items; they are checked on every element
+    like the others.  The oracle gets full-size host arrays in which only the
+    rows it reads are filled (the rest stay untouched zero pages)."""
     import bench
     print("gpu-generated case", cfg, flush=True)
     x = bench.gpu_inputs(cfg, seed=seed)
@@ -245,7 +248,12 @@ def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
     bt, tt = torch.from_numpy(rows // cfg.T), torch.from_numpy(rows % cfg.T)
     idx = idx_d.cpu().numpy()
     # tokens whose rows the oracle reads: the samples and every selector of the checked blocks
-    blocks = [N - 1 - i for i in blocks_from_end]
+    blocks = [N - 1 - i for i in list(blocks_from_end) + list(split_from_end)]
+    for i in split_from_end:
+        for g in range(cfg.G):
+            readers = int((idx[0, g] == N - 1 - i).any(axis=1).sum())
+            print("split block g=%d blk=%d: %d selecting tokens" % (g, N - 1 - i, readers), flush=True)
+            assert readers > BWD_ITEM_PAIRS, (g, N - 1 - i, readers)
     sel = np.zeros(cfg.T, dtype=bool)
     sel[rows % cfg.T] = True
     for g in range(cfg.G):
@@ -287,18 +295,20 @@ def _gpu_generated_check(msa, oracle_mod, cfg, n_rows, blocks_from_end, seed=0):
 
 
 def test_512k_config_gpu_generated(msa, oracle_mod):
-    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["512k"], n_rows=1024, blocks_from_end=[0, 2])
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["512k"], n_rows=1024, blocks_from_end=[0, 2],
+                         split_from_end=[800])
 
 
 def test_1m_config_gpu_generated(msa, oracle_mod):
-    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=1024, blocks_from_end=[0, 1])
+    _gpu_generated_check(msa, oracle_mod, synth.CONFIGS["1m"], n_rows=1024, blocks_from_end=[0, 1],
+                         split_from_end=[600])
 
 
 def test_max_topk_dense_128k_gpu_generated(msa, oracle_mod):
     """topk = 1024, the largest the boundary takes: at T = 131072 every query
     selects every causal block (dense causal attention through the sparse
     kernels).  Block 0 is then picked by all 131072 tokens, so its backward
-    list is cut into 32 items whose dK/dV are added atomically.  Checked on
+    list is cut into 128 items whose dK/dV are added atomically.  Checked on
     sampled rows and on late key blocks against the oracle."""
     cfg = synth.Config("128k-topk1024", 1, 131072, 8, 1, 128, 64, 1024)
     _gpu_generated_check(msa, oracle_mod, cfg, n_rows=32, blocks_from_end=[0, 1], seed=2)
