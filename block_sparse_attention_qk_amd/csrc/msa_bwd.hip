@@ -129,6 +129,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     // past the list reads the list's last entry (finite data, masked at store
     // time), list entries come from LDS, and scaling and validity are applied
     // when the staged registers go to LDS.
+    // Operand offsets of this lane: row l32's chunk 2ks + h is xq0 ^ 16ks
+    // (the swizzle is an XOR on the chunk bits), and key kown's P^T/dS^T run
+    // jj is xw0 ^ 8jj; the bases are made opaque per tile so that the eight
+    // offsets are formed next to their reads, not held in registers.
+    const int xq0 = l32 * D + 8 * swz<DCH>(l32, h), xw0 = kown * TR + 8 * pswz(kown, 0) + 4 * h;
     const int srow = tid >> 3, ssub = tid & 7;
     uint4 sq[2][CPT], sdo[2][CPT];
     int s_li[2] = {len, len}, s_ent[2] = {0, 0};
@@ -178,6 +183,11 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     for (int ks = 0; ks < KSD; ++ks) asm volatile("" : "+v"(bk[ks]), "+v"(bv[ks]));
     stage_load(I1{}, 1, list_entry(1));
     stage_load(I0{}, 2, list_entry(2));
+    // Drained once per item: the loop is then entered with no load in flight,
+    // so the compiler's waits inside it count only the loop's own staging
+    // loads (a load pending from here would make it wait for all of them at
+    // the loop head, once per six tiles).
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
 
     // One iteration: compute tile i+1, stage tile i+2, load tile i+4.  The
@@ -193,10 +203,12 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       if (i + 1 < ntiles) {
         const bf16raw* Qc = Qs[qb];
         const bf16raw* dOc = dOs[qb];
+        int xq = xq0, xw = xw0;
+        asm volatile("" : "+v"(xq), "+v"(xw));
         f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-          const int off = l32 * D + 8 * swz<DCH>(l32, 2 * ks + h);
+          const int off = xq ^ (16 * ks);
           sacc = mfma32(ld8(&Qc[off]), bk[ks], sacc);
           pacc = mfma32(ld8(&dOc[off]), bv[ks], pacc);
         }
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
             pv[ii] = !MASK || kown <= ma[ii] ? ex : 0.f;
             dsv[ii] = pv[ii] * fmaf(pacc[e], scale, -da[ii]);
           }
-          const int o = kown * TR + 8 * pswz(kown, jj) + 4 * h;
+          const int o = xw ^ (8 * jj);
           *reinterpret_cast<uint2*>(&PT[pb][o]) = make_uint2(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]));
           *reinterpret_cast<uint2*>(&dST[pb][o]) = make_uint2(pack2(dsv[0], dsv[1]), pack2(dsv[2], dsv[3]));
         }
@@ -246,10 +258,17 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
         produce(mc, I2{}, I1{}, I0{}, I0{}, i0 + 5);
       }
     };
-    if (it.w & ITEM_DIAG)
+    // Each loop drains its loads at its exit (two different wait forms, so that
+    // the two are not merged into one shared exit block): the loops share exit
+    // and entry checks, and a load of the masked loop still in flight on that
+    // path would make the compiler wait early inside the unmasked loop.
+    if (it.w & ITEM_DIAG) {
       loop(std::true_type{});
-    else
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    } else {
       loop(std::false_type{});
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    }
   } else {
     // =================== consumer ===================
     f32x16 dka[NCT], dva[NCT];
