@@ -122,20 +122,19 @@ __global__ __launch_bounds__(DTK_THREADS) void k_dec_topk(const float* __restric
   }
   const int nc = (L - 1) / BLK + 1, nsel = min(K, nc);
   const float* pr = pooled + (size_t)row * N;
+  // All loads in flight together: columns past the causal blocks read the
+  // last causal score (nc >= 1) and are masked after.
+  float sc[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) sc[i] = pr[min(i * DTK_THREADS + tid, nc - 1)];
   uint32_t key[VPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int col = i * DTK_THREADS + tid;
-    uint32_t kk = 0;
-    if (col < nc) {
-      float f = pr[col];
-      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
-      const uint32_t u = __float_as_uint(f);
-      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      kmin = min(kmin, kk);
-      kmax = max(kmax, kk);
-    }
+    const bool valid = i * DTK_THREADS + tid < nc;
+    const uint32_t kk = valid ? score_key(sc[i]) : 0u;
+    kmin = valid ? min(kmin, kk) : kmin;
+    kmax = valid ? max(kmax, kk) : kmax;
     key[i] = kk;
   }
 #pragma unroll

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
   __shared__ uint32_t red[2][TKW_WAVES];
   __shared__ uint32_t wsum[TKW_WAVES];
   __shared__ int bc[3];
-  __shared__ uint16_t ceq[VPT][TKW_WAVES], csel[VPT][TKW_WAVES];
+  constexpr int NW = VPT * TKW_THREADS / 32;  // bitmap words per row
+  __shared__ uint32_t gtw[NW], eqw[NW], wtot[TKW_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;  // the grid holds exactly the window's rows
   const int bg = row / W, t = t0 + row % W;
@@ -206,20 +207,19 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
   const float* pr = pooled + (size_t)row * N;
   int32_t* out = idx + ((size_t)bg * T + t) * K;
 
+  // All loads in flight together: columns past the causal blocks read the
+  // last causal score (nc >= 1) and are masked after.
+  float sc[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) sc[i] = pr[min(i * TKW_THREADS + tid, nc - 1)];
   uint32_t key[VPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int col = i * TKW_THREADS + tid;
-    uint32_t kk = 0;
-    if (col < nc) {
-      float f = pr[col];
-      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
-      const uint32_t u = __float_as_uint(f);
-      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      kmin = min(kmin, kk);
-      kmax = max(kmax, kk);
-    }
+    const bool valid = i * TKW_THREADS + tid < nc;
+    const uint32_t kk = valid ? score_key(sc[i]) : 0u;
+    kmin = valid ? min(kmin, kk) : kmin;
+    kmax = valid ? max(kmax, kk) : kmax;
     key[i] = kk;
   }
 #pragma unroll
@@ -308,50 +308,60 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
   const uint32_t kth = prefix;
   const int need_eq = all_eq ? INT_MAX : need;  // equal keys to take, lowest block index first
 
-  // Ascending write-out over columns i*512 + tid: per (column group, wave)
-  // counts of equal keys, then of chosen keys, each followed by one barrier.
-  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const bool eq = i * TKW_THREADS + tid < nc && key[i] == kth;
-    const unsigned long long meq = __ballot(eq);
-    if (lane == 0) ceq[i][wave] = (uint16_t)__popcll(meq);
-  }
-  __syncthreads();
-  bool selv[VPT];
-  int eq_base = 0;
+  // Ascending write-out from two bitmaps in LDS: word w holds columns
+  // 32w .. 32w+31, above (gtw) or equal to (eqw) the k-th key.  Columns
+  // i*512 + 64*wave + lane of one ballot are words 16i + 2*wave and the next.
+  // Thread tid < NW then owns word tid: one workgroup scan of the packed
+  // (above, equal) counts gives each word the chosen columns before it, since
+  // equal keys are taken lowest column first and need_eq of them in all.
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const bool valid = i * TKW_THREADS + tid < nc;
-    const bool eq = valid && key[i] == kth, gt = valid && key[i] > kth;
-    int before = eq_base, tot = 0;
-#pragma unroll
-    for (int w = 0; w < TKW_WAVES; ++w) {
-      const int cw = ceq[i][w];
-      before += w < wave ? cw : 0;
-      tot += cw;
+    const unsigned long long mg = __ballot(valid && key[i] > kth);
+    const unsigned long long me = __ballot(valid && key[i] == kth);
+    if (lane == 0) {
+      const int w = 16 * i + 2 * wave;
+      gtw[w] = (uint32_t)mg;
+      gtw[w + 1] = (uint32_t)(mg >> 32);
+      eqw[w] = (uint32_t)me;
+      eqw[w + 1] = (uint32_t)(me >> 32);
     }
-    const unsigned long long meq = __ballot(eq);
-    selv[i] = gt || (eq && before + __popcll(meq & lt) < need_eq);
-    const unsigned long long msel = __ballot(selv[i]);
-    if (lane == 0) csel[i][wave] = (uint16_t)__popcll(msel);
-    eq_base += tot;
   }
   __syncthreads();
-  int sel_base = 0;
+  const uint32_t gw = tid < NW ? gtw[tid] : 0u, ew = tid < NW ? eqw[tid] : 0u;
+  const uint32_t own = (uint32_t)__popc(gw) | ((uint32_t)__popc(ew) << 16);  // each count <= 8192
+  uint32_t incl = own;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    int before = sel_base, tot = 0;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
 #pragma unroll
-    for (int w = 0; w < TKW_WAVES; ++w) {
-      const int cw = csel[i][w];
-      before += w < wave ? cw : 0;
-      tot += cw;
+  for (int w = 0; w < TKW_WAVES; ++w)
+    if (w < wave) incl += wtot[w];
+  if (tid < NW) {
+    const uint32_t excl = incl - own;
+    const int gt_before = (int)(excl & 0xffffu), eq_before = (int)(excl >> 16);
+    const int take = need_eq - eq_before;  // equal keys of this word still wanted
+    uint32_t ek = 0u;
+    if (take >= __popc(ew)) {
+      ek = ew;
+    } else if (take > 0) {  // the lowest `take` set bits
+      uint32_t r = ew;
+      for (int j = 0; j < take; ++j) {
+        ek |= r & (0u - r);
+        r &= r - 1u;
+      }
     }
-    const unsigned long long msel = __ballot(selv[i]);
-    const int pos = before + __popcll(msel & lt);
-    if (selv[i] && pos < nsel) out[pos] = i * TKW_THREADS + tid;
-    sel_base += tot;
+    uint32_t ch = gw | ek;
+    int pos = gt_before + min(eq_before, need_eq);
+    while (ch != 0u) {
+      if (pos < nsel) out[pos] = 32 * tid + __ffs(ch) - 1;
+      ++pos;
+      ch &= ch - 1u;
+    }
   }
   for (int p = nsel + tid; p < K; p += TKW_THREADS) out[p] = -1;
 }

@@ -17,6 +17,13 @@ namespace msa {
 // tail is -1.
 constexpr int TOPK_BINS = 2048;
 
+// Order-preserving u32 key of a score; -0 ranks equal to +0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Writes the nsel = min(K, nc) best of the nc scores pr[0..nc) to out[0..nsel)
 // in ascending block order and -1 to out[nsel..K).  `hist` is TOPK_BINS words
 // of this wave's LDS.  All 64 lanes must call it together.
@@ -25,19 +32,14 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
                                          uint32_t* hist, int lane) {
   const int nsel = min(K, nc);
 
+  // Every load is issued before the first is used: columns past the row's
+  // causal blocks read its last causal score (nc >= 1) and are masked after.
+  float sc[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) sc[i] = pr[min(i * 64 + lane, nc - 1)];
   uint32_t key[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int col = i * 64 + lane;
-    uint32_t kk = 0;
-    if (col < nc) {
-      float f = pr[col];
-      if (f == 0.0f) f = 0.0f;  // -0 ranks equal to +0
-      const uint32_t u = __float_as_uint(f);
-      kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    key[i] = kk;
-  }
+  for (int i = 0; i < VPL; ++i) key[i] = i * 64 + lane < nc ? score_key(sc[i]) : 0u;
 
   uint32_t prefix = 0;
   int need = nsel;      // rank of the wanted key among keys matching prefix
