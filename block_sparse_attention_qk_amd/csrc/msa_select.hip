@@ -92,13 +92,23 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
       __builtin_amdgcn_global_load_lds(src, slot + (NDMA * wave + u) * 512, 16, 0, 0);
     }
   };
+  // Thread i writes block kb0 + i % 8 of the rows i / 8 + 64j.  Its row base is
+  // formed here from an opaque copy of the thread index: held across the key
+  // loop, it would be spilled, and reloading it would wait for the ring copies.
   auto flush = [&](int chunk) {  // pooled blocks [chunk*8, chunk*8+8) of the 256 queries
+    constexpr int RSTEP = 64 * POOL_WAVES / POOL_CHB;
     const int kb0 = chunk * POOL_CHB;
     const float* pb = pbuf[chunk & 1];
-    for (int i = threadIdx.x; i < POOL_QT * POOL_CHB; i += 64 * POOL_WAVES) {
-      const int r = i / POOL_CHB, c = i % POOL_CHB, t = qt0 + r;
-      if (kb0 + c <= kb_last && t <= qlast && kb0 + c <= t / BLK)
-        pooled[((size_t)bg * W + (t - t0)) * N + kb0 + c] = pb[r * PST + c];
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int c = tid % POOL_CHB, r0 = tid / POOL_CHB;
+    if (kb0 + c <= kb_last) {
+      float* dst = pooled + ((size_t)bg * W + (qt0 + r0 - t0)) * N + kb0 + c;
+#pragma unroll
+      for (int j = 0; j < POOL_QT / RSTEP; ++j) {
+        const int r = r0 + RSTEP * j, t = qt0 + r;
+        if (t <= qlast && kb0 + c <= t / BLK) dst[(size_t)RSTEP * j * N] = pb[r * PST + c];
+      }
     }
   };
 
