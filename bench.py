@@ -51,7 +51,7 @@ METRIC = "MSA fwd+bwd tokens/s and effective TFLOP/s (% bf16 MFMA peak), 128K & 
 # Library timing slot -> kernel symbol prefix and the source file it is built from.
 KERNELS = {  # bench name -> (kernel symbol in rocprofv3 output, source files it is compiled from)
     "proxy_pool": ("msa::k_proxy_pool<", ("msa_select.hip",)),
-    "topk": ("msa::k_topk<", ("msa_select.hip", "msa_topk.h")),
+    "topk": ("msa::k_topk", ("msa_select.hip", "msa_topk.h")),  # k_topk and k_topk_wg
     "inverse": ("msa::k_inv_scatter", ("msa_inverse.hip",)),
     "fwd_partials": ("msa::k_fwd_kv<", ("msa_fwd.hip",)),
     "fwd_combine": ("msa::k_fwd_combine<", ("msa_fwd.hip",)),
