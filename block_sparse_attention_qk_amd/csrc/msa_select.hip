@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
 // and the same tie rule (keys equal to the k-th taken lowest block first).
 constexpr int TKW_THREADS = 512;
 constexpr int TKW_WAVES = TKW_THREADS / 64;
+constexpr int TKW_CAND = 256;  // largest chosen linear bin ranked directly
 
 template <int VPT>
 __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict__ pooled,
@@ -208,6 +209,8 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
   __shared__ uint32_t red[2][TKW_WAVES];
   __shared__ uint32_t wsum[TKW_WAVES];
   __shared__ int bc[3];
+  __shared__ uint32_t cand[TKW_CAND];  // keys of the chosen linear bin
+  __shared__ int ncand, kq[2];
   constexpr int NW = VPT * TKW_THREADS / 32;  // bitmap words per row
   __shared__ uint32_t gtw[NW], eqw[NW], wtot[TKW_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -249,23 +252,11 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
     kmin = min(kmin, red[0][w]);
     kmax = max(kmax, red[1][w]);
   }
-  // Radix select of the nsel-th largest key below the common prefix of kmin and kmax.
-  const uint32_t diff = kmin ^ kmax;
-  int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);
-  uint32_t prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
-  int need = nsel;      // rank of the wanted key among the keys matching prefix
-  bool all_eq = false;  // every key equal to the final prefix is taken
-  while (bits > 0) {    // bits, prefix and need are the same in every thread
-    const int width = bits < 11 ? bits : 11;
-    const int sh = bits - width, nbins = 1 << width;
-    const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
-    for (int j = tid; j < nbins; j += TKW_THREADS) hist[j] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (i * TKW_THREADS + tid < nc && (key[i] & hi_mask) == prefix)
-        atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
-    __syncthreads();
+  // The chosen bin of a histogram whose counts are in hist[0..nbins): the bin
+  // holding the need-th largest key, counted from the top.  Writes bc = {bin,
+  // rank of the wanted key inside the bin, the bin's count}; all threads read
+  // bc after the second barrier (hist and wsum are next written after it).
+  auto scan_bin = [&](int nbins, int need) {
     // thread tid owns the bins [top - PER, top) counted from the top bin down
     const int top = nbins - PER * tid;
     uint32_t c[PER], lsum = 0;
@@ -304,19 +295,100 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
       bc[2] = (int)cbin;
     }
     __syncthreads();
-    prefix |= (uint32_t)bc[0] << sh;
-    need = bc[1];
-    bits = sh;
-    // The chosen bin holds exactly the keys still needed: all of them are taken,
-    // the lower digits cannot change that, and no other key ties with them.
-    if (bc[2] == need) {
-      all_eq = true;
-      break;
+  };
+
+  uint32_t kth = 0u;
+  int need_eq = 0;  // equal keys to take, lowest block index first
+  bool done = false;
+  if (nsel == nc) {  // every causal block is taken
+    kth = kmin;
+    need_eq = INT_MAX;
+    done = true;
+  } else {
+    // First digit: 2048 bins spread linearly between the row's smallest and
+    // largest score.  The bin is a non-decreasing function of the score, so
+    // the wanted key lies in the chosen bin and every key of a higher bin is
+    // larger.  Scores cluster far less in the upper tail than in the float
+    // exponent, so the chosen bin holds a few keys, ranked directly.  Rows with
+    // non-finite scores, equal extremes or a crowded bin take the radix path.
+    const float fmin = key_score(kmin), fmax = key_score(kmax);
+    const float span = fmax - fmin, scl = (float)TOPK_BINS / span;
+    if (fmax > fmin && __builtin_isfinite(span) && __builtin_isfinite(scl) && scl > 0.f) {  // same in every thread
+      int lb[VPT];
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        lb[i] = i * TKW_THREADS + tid < nc ? min(TOPK_BINS - 1, (int)((sc[i] - fmin) * scl)) : -1;
+      for (int j = tid; j < TOPK_BINS; j += TKW_THREADS) hist[j] = 0;
+      if (tid == 0) {
+        ncand = 0;
+        kq[0] = (int)kmax;  // replaced below by the one key that satisfies the rank test
+        kq[1] = 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (lb[i] >= 0) atomicAdd(&hist[lb[i]], 1u);
+      __syncthreads();
+      scan_bin(TOPK_BINS, nsel);
+      const int b = bc[0], needb = bc[1], cntb = bc[2];
+      if (cntb <= TKW_CAND) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          if (lb[i] == b) cand[atomicAdd(&ncand, 1)] = key[i];
+        __syncthreads();
+        if (tid < cntb) {  // the candidate whose key has needb - 1 larger ones and needb or more at least as large
+          const uint32_t mine = cand[tid];
+          int gt = 0, ge = 0;
+          for (int j = 0; j < cntb; ++j) {
+            const uint32_t o = cand[j];
+            gt += o > mine;
+            ge += o >= mine;
+          }
+          if (gt < needb && needb <= ge) {  // the same values from every candidate equal to it
+            kq[0] = (int)mine;
+            kq[1] = needb - gt;
+          }
+        }
+        __syncthreads();
+        kth = (uint32_t)kq[0];
+        need_eq = kq[1];
+        done = true;
+      }
     }
-    // hist, wsum and bc are next written after two more barriers: no barrier here
   }
-  const uint32_t kth = prefix;
-  const int need_eq = all_eq ? INT_MAX : need;  // equal keys to take, lowest block index first
+  if (!done) {
+    // Radix select of the nsel-th largest key below the common prefix of kmin and kmax.
+    const uint32_t diff = kmin ^ kmax;
+    int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);
+    uint32_t prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
+    int need = nsel;      // rank of the wanted key among the keys matching prefix
+    bool all_eq = false;  // every key equal to the final prefix is taken
+    while (bits > 0) {    // bits, prefix and need are the same in every thread
+      const int width = bits < 11 ? bits : 11;
+      const int sh = bits - width, nbins = 1 << width;
+      const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
+      for (int j = tid; j < nbins; j += TKW_THREADS) hist[j] = 0;
+      __syncthreads();
+  #pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (i * TKW_THREADS + tid < nc && (key[i] & hi_mask) == prefix)
+          atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
+      __syncthreads();
+      scan_bin(nbins, need);
+      prefix |= (uint32_t)bc[0] << sh;
+      need = bc[1];
+      bits = sh;
+      // The chosen bin holds exactly the keys still needed: all of them are taken,
+      // the lower digits cannot change that, and no other key ties with them.
+      if (bc[2] == need) {
+        all_eq = true;
+        break;
+      }
+      // hist, wsum and bc are next written after two more barriers: no barrier here
+    }
+    kth = prefix;
+    need_eq = all_eq ? INT_MAX : need;
+  }
 
   // Ascending write-out from two bitmaps in LDS: word w holds columns
   // 32w .. 32w+31, above (gtw) or equal to (eqw) the k-th key.  Columns
@@ -368,7 +440,7 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
     uint32_t ch = gw | ek;
     int pos = gt_before + min(eq_before, need_eq);
     while (ch != 0u) {
-      if (pos < nsel) out[pos] = 32 * tid + __ffs(ch) - 1;
+      if ((unsigned)pos < (unsigned)nsel) out[pos] = 32 * tid + __ffs(ch) - 1;
       ++pos;
       ch &= ch - 1u;
     }

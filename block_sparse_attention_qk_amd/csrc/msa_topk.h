@@ -24,6 +24,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score of a key (the inverse of score_key; -0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Writes the nsel = min(K, nc) best of the nc scores pr[0..nc) to out[0..nsel)
 // in ascending block order and -1 to out[nsel..K).  `hist` is TOPK_BINS words
 // of this wave's LDS.  All 64 lanes must call it together.
