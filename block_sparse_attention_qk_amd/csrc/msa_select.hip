@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
 template <int VPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, int32_t* __restrict__ idx,
                                               int T, int N, int K, int t0, int W, int rows) {
-  __shared__ uint32_t hist_all[4][TOPK_BINS];
+  __shared__ uint32_t hist_all[4][TOPK_ROW_LDS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;  // whole wave exits: no block-level barrier below

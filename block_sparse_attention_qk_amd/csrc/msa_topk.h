@@ -7,15 +7,17 @@
 
 namespace msa {
 
-// Top-k of one pooled row per wavefront.  Scores become order-preserving u32
-// keys held in registers (VPL per lane).  The k-th largest key is found by a
-// three-digit radix select (11, 11 and 10 bits): each digit is histogrammed in
-// LDS over the keys that match the digits found so far, and a wave scan from
-// the top bin finds the bin where the count of larger keys reaches k.  Blocks
-// above the k-th key are taken, then blocks equal to it lowest index first;
-// a ballot pass writes the chosen block ids in ascending order, and the row
-// tail is -1.
+// Top-k of one pooled row per wavefront (rows of at most 1024 blocks).  Scores
+// become order-preserving u32 keys held in registers (VPL per lane).  The k-th
+// largest key is found from a histogram of 256 bins spread linearly between
+// the row's smallest and largest score: the chosen bin's few keys are ranked
+// directly.  Rows with non-finite or equal extreme scores, or a crowded bin,
+// build the k-th key bit by bit instead.  Blocks above the k-th key are taken,
+// then blocks equal to it lowest index first; a ballot pass writes the chosen
+// block ids in ascending order, and the row tail is -1.
 constexpr int TOPK_BINS = 2048;
+constexpr int TOPK_LIN_BINS = 256;                     // linear first digit of rows up to 1024 blocks
+constexpr int TOPK_ROW_LDS = TOPK_LIN_BINS + 64;        // LDS words per wave: bins, then the chosen bin's keys
 
 // Order-preserving u32 key of a score; -0 ranks equal to +0.
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -30,7 +32,7 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 }
 
 // Writes the nsel = min(K, nc) best of the nc scores pr[0..nc) to out[0..nsel)
-// in ascending block order and -1 to out[nsel..K).  `hist` is TOPK_BINS words
+// in ascending block order and -1 to out[nsel..K).  `hist` is TOPK_ROW_LDS words
 // of this wave's LDS.  All 64 lanes must call it together.
 template <int VPL>
 __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, int K, int32_t* __restrict__ out,
@@ -46,89 +48,52 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
 #pragma unroll
   for (int i = 0; i < VPL; ++i) key[i] = i * 64 + lane < nc ? score_key(sc[i]) : 0u;
 
+  static_assert(VPL <= 16, "rows of more than 1024 blocks take the workgroup kernel");
   uint32_t prefix = 0;
-  int need = nsel;      // rank of the wanted key among keys matching prefix
-  bool all_eq = false;  // every key equal to the final prefix is taken
-  if constexpr (VPL <= 16) {
-    // Short rows: build the k-th largest key bit by bit from the top; each
-    // step is one ballot count per register of keys.  The bits that the row's
-    // smallest and largest keys share are taken as they are (every key has
-    // them), and the search stops once exactly nsel keys lie at or above the
-    // prefix: the lower bits could then no longer change which keys are
-    // chosen, and no unchosen key equals a chosen one.
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
+  int need = nsel;  // equal keys to take, lowest block index first
+  uint32_t kmin = 0xffffffffu, kmax = 0u;  // over the row's causal blocks
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (i * 64 + lane < nc) {
-        kmin = min(kmin, key[i]);
-        kmax = max(kmax, key[i]);
-      }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-    }
-    const uint32_t diff = kmin ^ kmax;
-    int bit = diff == 0u ? -1 : 31 - __builtin_clz(diff);  // highest bit not shared by all keys
-    prefix = bit < 0 ? kmax : (bit == 31 ? 0u : kmax & ~((2u << bit) - 1u));
-    int cge = nc;  // keys at or above prefix
-    for (; bit >= 0 && cge != nsel; --bit) {
-      const uint32_t cand = prefix | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i * 64 < nc) cnt += __popcll(__ballot((i * 64 + lane < nc) && key[i] >= cand));
-      if (cnt >= nsel) {
-        prefix = cand;
-        cge = cnt;
-      }
-    }
-    int cnt_gt = 0;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (i * 64 < nc) cnt_gt += __popcll(__ballot((i * 64 + lane < nc) && key[i] > prefix));
-    need = nsel - cnt_gt;
-  } else {
-  // Radix select of the nsel-th largest key.  Pooled scores of a row share
-  // their sign and exponent bits, so the digits start below the common prefix
-  // of the row's smallest and largest key (otherwise every key would fall into
-  // one histogram bin).
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i * 64 >= nc) break;
+  for (int i = 0; i < VPL; ++i)
     if (i * 64 + lane < nc) {
       kmin = min(kmin, key[i]);
       kmax = max(kmax, key[i]);
     }
-  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
   }
-  const uint32_t diff = kmin ^ kmax;
-  int bits = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // low bits still undecided
-  prefix = bits == 32 ? 0u : (kmax & ~((1u << bits) - 1u));
-  while (bits > 0) {
-    const int width = bits < 11 ? bits : 11;
-    const int sh = bits - width, nbins = 1 << width;
-    const uint32_t hi_mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
-    for (int j = lane; j < nbins; j += 64) hist[j] = 0;
+  // First, when the row's scores are finite and not all equal: 256 bins
+  // spread linearly between its smallest and largest score.  The bin is a
+  // non-decreasing function of the score, so the k-th key lies in the chosen
+  // bin and every key of a higher bin is larger; the chosen bin holds a few
+  // keys, ranked directly.  A row that takes every causal block needs no
+  // search (its k-th key is the smallest).
+  bool found = nsel == nc;
+  if (found) prefix = kmin;
+  const float fmin = key_score(kmin), fmax = key_score(kmax);
+  const float span = fmax - fmin, scl = (float)TOPK_LIN_BINS / span;
+  if (!found && fmax > fmin && __builtin_isfinite(span) && __builtin_isfinite(scl) && scl > 0.f) {
+    constexpr int PERL = TOPK_LIN_BINS / 64;  // bins per lane in the scan
+    int lb[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      lb[i] = i * 64 + lane < nc ? min(TOPK_LIN_BINS - 1, (int)((sc[i] - fmin) * scl)) : -1;
+#pragma unroll
+    for (int j = 0; j < PERL; ++j) hist[lane + 64 * j] = 0;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (i * 64 >= nc) break;
-      if (i * 64 + lane < nc && (key[i] & hi_mask) == prefix)
-        atomicAdd(&hist[(key[i] >> sh) & (nbins - 1)], 1u);
-    }
+    for (int i = 0; i < VPL; ++i)
+      if (lb[i] >= 0) atomicAdd(&hist[lb[i]], 1u);
     __builtin_amdgcn_wave_barrier();
-    // lanes own `per` consecutive bins each, scanned from the top bin down
-    const int per = nbins >= 64 ? nbins / 64 : 1;
-    const int top = nbins - per * lane;
-    uint32_t lsum = 0;
-    if (top > 0)
-      for (int j = 0; j < per; ++j) lsum += hist[top - 1 - j];
+    // lane owns bins [top - PERL, top) counted from the top bin down
+    const int top = TOPK_LIN_BINS - PERL * lane;
+    uint32_t c[PERL], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < PERL; ++j) {
+      c[j] = hist[top - 1 - j];
+      lsum += c[j];
+    }
     uint32_t incl = lsum;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -136,35 +101,82 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ pr, int nc, i
       if (lane >= off) incl += o;
     }
     const uint32_t excl = incl - lsum;
-    const unsigned long long hit = __ballot(top > 0 && excl < (uint32_t)need && (uint32_t)need <= incl);
-    const int owner = __builtin_ctzll(hit);
-    uint32_t run = __shfl(excl, owner);
-    const int otop = nbins - per * owner;
-    int bin = otop - 1;
-    uint32_t cbin = 0;  // keys in the chosen bin
-    for (int j = 0; j < per; ++j) {  // every lane walks the owner's bins (LDS broadcast)
-      const uint32_t c = hist[otop - 1 - j];
-      if (run + c >= (uint32_t)need) {
-        bin = otop - 1 - j;
-        cbin = c;
-        break;
+    int bin = -1, nb = 0, cb = 0;  // chosen bin, rank of the k-th key in it, its count (owner lane)
+    if (excl < (uint32_t)nsel && (uint32_t)nsel <= incl) {
+      uint32_t run = excl;
+#pragma unroll
+      for (int j = 0; j < PERL; ++j) {
+        if (bin < 0 && run + c[j] >= (uint32_t)nsel) {
+          bin = top - 1 - j;
+          nb = nsel - (int)run;
+          cb = (int)c[j];
+        }
+        run += c[j];
       }
-      run += c;
     }
-    need -= (int)run;
-    prefix |= (uint32_t)bin << sh;
-    bits = sh;
-    // The chosen bin holds exactly the keys still needed: all of them are taken,
-    // the lower digits cannot change that, and no other key ties with them.
-    if (cbin == (uint32_t)need) {
-      all_eq = true;
-      break;
+    const int owner = __builtin_ctzll(__ballot(bin >= 0));
+    bin = __shfl(bin, owner);
+    nb = __shfl(nb, owner);
+    cb = __shfl(cb, owner);
+    if (cb <= 64) {  // gather the bin's keys after the bins, then rank them
+      uint32_t* cand = hist + TOPK_LIN_BINS;
+      const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const unsigned long long m = __ballot(lb[i] == bin);
+        if (lb[i] == bin) cand[base + __popcll(m & lt)] = key[i];
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_wave_barrier();
+      bool hit = false;
+      uint32_t mine = 0u;
+      if (lane < cb) {  // the key with fewer than nb larger and at least nb at least as large
+        mine = cand[lane];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < cb; ++j) {
+          const uint32_t o = cand[j];
+          gt += o > mine;
+          ge += o >= mine;
+        }
+        hit = gt < nb && nb <= ge;
+      }
+      const unsigned long long hm = __ballot(hit);
+      if (hm != 0ull) {
+        prefix = (uint32_t)__shfl((int)mine, __builtin_ctzll(hm));
+        found = true;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
+  // Otherwise build the k-th largest key bit by bit from the top; each step
+  // is one ballot count per register of keys.  The bits that the row's
+  // smallest and largest keys share are taken as they are (every key has
+  // them), and the search stops once exactly nsel keys lie at or above the
+  // prefix: the lower bits could then no longer change which keys are
+  // chosen, and no unchosen key equals a chosen one.
+  const uint32_t diff = kmin ^ kmax;
+  int bit = found ? -1 : (diff == 0u ? -1 : 31 - __builtin_clz(diff));  // highest bit not shared by all keys
+  if (!found) prefix = bit < 0 ? kmax : (bit == 31 ? 0u : kmax & ~((2u << bit) - 1u));
+  int cge = nc;  // keys at or above prefix
+  for (; bit >= 0 && cge != nsel; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i * 64 < nc) cnt += __popcll(__ballot((i * 64 + lane < nc) && key[i] >= cand));
+    if (cnt >= nsel) {
+      prefix = cand;
+      cge = cnt;
+    }
   }
+  int cnt_gt = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (i * 64 < nc) cnt_gt += __popcll(__ballot((i * 64 + lane < nc) && key[i] > prefix));
+  need = nsel - cnt_gt;
   const uint32_t kth = prefix;
-  const int need_eq = all_eq ? INT_MAX : need;  // equal keys to take, lowest block index first
+  const int need_eq = need;
 
   const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int run_eq = 0, run_sel = 0;

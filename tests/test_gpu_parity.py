@@ -334,6 +334,27 @@ def test_long_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
 
 
+@pytest.mark.parametrize("T,topk", [(1 << 14, 16), (1 << 17, 32)])
+def test_short_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
+    """Rows of at most 1024 blocks go through one wave per row.  With one
+    128-row proxy-key block repeated, every complete block has the same pooled
+    score: the chosen linear bin is crowded (or the row is all equal), so the
+    bit-by-bit search decides, and the lowest block ids must win."""
+    print("short-row ties", T, topk, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(23)
+    base = torch.randn((128, G, dp), generator=g).to(torch.bfloat16)
+    kp = base.repeat(T // 128, 1, 1).unsqueeze(0).contiguous()
+    qp = torch.randn((1, T, G, dp), generator=g).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([T - 1, T - 200, T // 2 + 77, 40 * 128 + 5, 20 * 128 + 127, 3 * 128 + 1])
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
 @pytest.mark.parametrize("T,G,topk,n_rows", [(1 << 18, 2, 64, 1536), (1 << 20, 1, 288, 384)])
 def test_long_rows_many_rows_match_oracle(msa, oracle_mod, T, G, topk, n_rows):
     """Rows longer than 1024 blocks are selected by one workgroup per row.
