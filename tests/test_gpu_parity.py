@@ -355,6 +355,31 @@ def test_short_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk)
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
 
 
+@pytest.mark.parametrize("T,topk", [(1 << 17, 4), (1 << 17, 32), (1 << 18, 4), (1 << 18, 40)])
+def test_infinite_scores_match_oracle(msa, oracle_mod, T, topk):
+    """Proxy keys of +-3e38 against positive proxy queries score +inf (blocks 5
+    and 9) or -inf (block 2) in fp32 on both sides.  Rows with an infinite
+    smallest or largest score cannot be binned linearly: they take the
+    bit-by-bit search (rows of 1024 blocks) or the radix passes (2048 blocks),
+    and infinite scores tie to the lower block like any other."""
+    print("infinite scores", T, topk, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(29)
+    kp = torch.randn((1, T, G, dp), generator=g)
+    kp[0, 2 * 128:3 * 128] = -3e38
+    kp[0, 5 * 128:6 * 128] = 3e38
+    kp[0, 9 * 128:10 * 128] = 3e38
+    kp = kp.to(torch.bfloat16)
+    qp = (torch.rand((1, T, G, dp), generator=g) + 0.5).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([4 * 128 + 17, 6 * 128 + 3, 10 * 128 + 50, T // 2 + 77, T - 1])
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
 @pytest.mark.parametrize("T,G,topk,n_rows", [(1 << 18, 2, 64, 1536), (1 << 20, 1, 288, 384)])
 def test_long_rows_many_rows_match_oracle(msa, oracle_mod, T, G, topk, n_rows):
     """Rows longer than 1024 blocks are selected by one workgroup per row.
