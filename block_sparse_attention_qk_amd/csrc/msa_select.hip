@@ -128,12 +128,21 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
     // the wave crosses (all but the last one or two) take only the maxima.
     auto tiles = [&](auto maskc) {
       constexpr bool MASK = decltype(maskc)::value;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {  // 32-key tiles (other waves of the SIMD cover the MFMA chain)
-        f32x16 acc = zero16();
+      // The operands of tile mt+1 are read before the MFMAs of tile mt, into the
+      // other of two register sets, so each tile's reads have a tile's work to land.
+      bf16x8 ka[2][KS];
+      auto rd = [&](int mt, int set) {
         const int r = 32 * mt + l32;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(&kc[r * DP + 8 * kswz<DP>(r, 2 * ks + h)]), bq[ks], acc);
+        for (int ks = 0; ks < KS; ++ks) ka[set][ks] = ld8(&kc[r * DP + 8 * kswz<DP>(r, 2 * ks + h)]);
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {  // 32-key tiles (other waves of the SIMD cover the MFMA chain)
+        if (mt + 1 < 4) rd(mt + 1, (mt + 1) & 1);
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[mt & 1][ks], bq[ks], acc);
         // lane holds query column l32 and keys 32mt + 8(e/4) + 4h + e%4
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
