@@ -201,10 +201,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ pooled, 
 // keys per thread in columns i*512 + tid.  A wave per row would need 64 key
 // registers or more per lane at these lengths (one wave per SIMD, spilled
 // scalars); here each thread holds at most 16 keys and eight waves share the
-// radix select: the same digits as the wave routine (11 bits below the row's
-// common prefix), histograms in LDS, a workgroup scan from the top bin, the
-// same early stop when the chosen bin holds exactly the keys still needed,
-// and the same tie rule (keys equal to the k-th taken lowest block first).
+// search for the k-th key: a histogram of 2048 bins spread linearly between
+// the row's smallest and largest score, with the chosen bin's few keys ranked
+// directly, else a radix select (11-bit digits below the row's common prefix,
+// a workgroup scan from the top bin, an early stop when the chosen bin holds
+// exactly the keys still needed).  The tie rule is the wave routine's: keys
+// equal to the k-th are taken lowest block first.
 constexpr int TKW_THREADS = 512;
 constexpr int TKW_WAVES = TKW_THREADS / 64;
 constexpr int TKW_CAND = 256;  // largest chosen linear bin ranked directly
