@@ -1,5 +1,6 @@
-// Per-row top-k of pooled block scores, one row per wavefront, shared by the
-// training-shape and decode-shape Index Branch kernels.
+// Per-row top-k of pooled block scores: the order-preserving score keys and
+// histogram sizes shared by the training and decode Index Branch kernels, and
+// the one-wave-per-row routine of the training kernel for rows up to 1024 blocks.
 #pragma once
 #include <climits>
 
