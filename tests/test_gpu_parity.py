@@ -380,6 +380,36 @@ def test_infinite_scores_match_oracle(msa, oracle_mod, T, topk):
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
 
 
+@pytest.mark.parametrize("mode", ["decades", "outlier"])
+@pytest.mark.parametrize("T,topk", [(1 << 17, 32), (1 << 19, 64)])
+def test_wide_score_range_matches_oracle(msa, oracle_mod, T, topk, mode):
+    """Rows whose scores span a wide range, against the oracle (rows of 1024
+    blocks: one wave per row; 4096 blocks: a workgroup per row).  "decades":
+    proxy-key blocks scaled by 10^u, u uniform in [-3, 3]; the k-th key's linear
+    bin holds a few to a few dozen keys, ranked directly.  "outlier": block 3
+    scaled by 1e5 and the rest by 1, so every other score falls into the lowest
+    linear bins and the chosen bin is crowded: the radix or bit-by-bit search
+    decides."""
+    print("wide score range", T, topk, mode, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(31)
+    N = T // 128
+    if mode == "decades":
+        scale = torch.pow(10.0, torch.rand((N,), generator=g) * 6 - 3)
+    else:
+        scale = torch.ones((N,))
+        scale[3] = 1e5
+    kp = (torch.randn((1, T, G, dp), generator=g) * scale.repeat_interleave(128)[None, :, None, None]).to(torch.bfloat16)
+    qp = torch.randn((1, T, G, dp), generator=g).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([T - 1, T - 300, T // 2 + 11, T // 4 + 129, 50 * 128 + 7, 5 * 128 + 64])
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
 @pytest.mark.parametrize("T,G,topk,n_rows", [(1 << 18, 2, 64, 1536), (1 << 20, 1, 288, 384)])
 def test_long_rows_many_rows_match_oracle(msa, oracle_mod, T, G, topk, n_rows):
     """Rows longer than 1024 blocks are selected by one workgroup per row.
