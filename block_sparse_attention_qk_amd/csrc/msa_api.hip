@@ -29,9 +29,9 @@ struct Layout {
   int W = 0;
   size_t total = 0;
   size_t pooled = 0;
-  size_t counts = 0, base = 0, len = 0, items = 0, item_count = 0, list = 0;
+  size_t counts = 0, base = 0, len = 0, items = 0, item_count = 0, list = 0, order = 0;
   int max_items = 0;
-  size_t items2 = 0, item_count2 = 0;  // merged call: backward items cut from the same inverse index
+  size_t items2 = 0, item_count2 = 0, order2 = 0;  // merged call: backward items cut from the same inverse index
   int max_items2 = 0;
   size_t part_o = 0, part_lse = 0;
   size_t Dd = 0, dk_acc = 0, dv_acc = 0, dq_part = 0;
@@ -56,6 +56,7 @@ void carve_inverse(Layout& L, Carver& c, const Geo& g, int W, int item_tokens) {
   L.items = c.take(BG * (size_t)L.max_items * 16);
   L.item_count = c.take(BG * 4);
   L.list = c.take(BG * (size_t)W * g.K * 4);
+  L.order = c.take(BG * (size_t)L.max_items * 4);
 }
 
 Layout layout(const Geo& g, msa_op op, int W) {
@@ -82,6 +83,7 @@ Layout layout(const Geo& g, msa_op op, int W) {
     L.max_items2 = inv_max_items(g, W, BWD_ITEM_TOKENS);
     L.items2 = c.take(BG * (size_t)L.max_items2 * 16);
     L.item_count2 = c.take(BG * 4);
+    L.order2 = c.take(BG * (size_t)L.max_items2 * 4);
     L.part_lse = c.take((pairs + 1) * g.R * 4);
     L.part_o = c.take((pairs + 1) * g.R * g.D * 2);
     L.dq_part = L.part_o;
@@ -177,6 +179,7 @@ InvBufs inv_bufs(const Layout& L, char* ws) {
   ib.items = reinterpret_cast<int4*>(ws + L.items);
   ib.item_count = reinterpret_cast<int32_t*>(ws + L.item_count);
   ib.list = reinterpret_cast<int32_t*>(ws + L.list);
+  ib.order = reinterpret_cast<int32_t*>(ws + L.order);
   ib.max_items = L.max_items;
   return ib;
 }
@@ -434,6 +437,7 @@ msa_status msa_fwd_bwd(const msa_dims* dims, const msa_bf16* q, const msa_bf16* 
   InvBufs ib2 = ib;  // same list, backward-sized items
   ib2.items = reinterpret_cast<int4*>(base + L.items2);
   ib2.item_count = reinterpret_cast<int32_t*>(base + L.item_count2);
+  ib2.order = reinterpret_cast<int32_t*>(base + L.order2);
   ib2.max_items = L.max_items2;
   float* Dd = reinterpret_cast<float*>(base + L.Dd);
   float* dk_acc = reinterpret_cast<float*>(base + L.dk_acc);

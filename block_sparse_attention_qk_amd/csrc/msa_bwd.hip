@@ -17,6 +17,7 @@
 // triple-buffered in LDS, P^T/dS^T double-buffered; every LDS tile is
 // XOR-swizzled on 16-byte chunks (v_mfma_f32_32x32x16_bf16 operands by 16-byte
 // reads and by ds_read_b64_tr_b16 transpose reads).
+// Items are dispatched in the order of their first token.
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
 // token's partials.  dK/dV are added into fp32 accumulators once per item
 // (atomically only when a block's list is cut into several items).
@@ -50,8 +51,8 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     const bf16raw* __restrict__ q, const bf16raw* __restrict__ k, const bf16raw* __restrict__ v,
     const bf16raw* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int4* __restrict__ items, const int32_t* __restrict__ item_count, const int32_t* __restrict__ list,
-    bf16raw* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc, int T, int H, int G,
-    int K, int t0, int W, int max_items, float scale, float sl2) {
+    const int32_t* __restrict__ order, bf16raw* __restrict__ dq_part, float* __restrict__ dk_acc,
+    float* __restrict__ dv_acc, int T, int H, int G, int K, int t0, int W, int max_items, float scale, float sl2) {
   constexpr int KSD = D / 16;    // 32x32x16 k-steps over the head dim
   constexpr int NCT = D / 32;    // 32-wide head-dim tiles
   constexpr int DCH = D / 8;     // 16-byte chunks per row
@@ -69,12 +70,15 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) int rpair[3][TR];
   __shared__ int lsts[BWD_ITEM_TOKENS];  // the item's pair list
 
-  // Groups run one after another in dispatch order: the query rows that the
-  // running items re-read are one group's, which the last-level cache holds
-  // better than all groups' (items are capped at BWD_ITEM_TOKENS pairs, so no
-  // single item dominates the tail).
-  const int bg = (int)blockIdx.x / max_items, item = (int)blockIdx.x % max_items;
-  if (item >= item_count[bg]) return;
+  // Groups run one after another in dispatch order, and a group's items in
+  // the order of their first token (k_item_order): the query and dO rows that
+  // the running items gather then come from one group and a narrow token
+  // range, which the last-level cache holds far better than all of a group's
+  // rows (items are capped at BWD_ITEM_TOKENS pairs, so no single item
+  // dominates the tail).
+  const int bg = (int)blockIdx.x / max_items, slot = (int)blockIdx.x % max_items;
+  if (slot >= item_count[bg]) return;
+  const int item = order[(size_t)bg * max_items + slot];
   const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
@@ -494,14 +498,53 @@ __global__ __launch_bounds__(256) void k_cvt_bf16(const float4* __restrict__ src
   }
 }
 
+// Dispatch order of a (batch, group)'s backward items: by the first token of
+// their run (a counting sort into ORD_BINS token buckets), so that the items
+// running at one time gather query and dO rows from a narrow token range.
+constexpr int ORD_THREADS = 1024, ORD_BINS = 1024;
+__global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restrict__ items,
+                                                           const int32_t* __restrict__ item_count,
+                                                           const int32_t* __restrict__ list, int32_t* __restrict__ order,
+                                                           int max_items, int K, int W) {
+  __shared__ int cnt[ORD_BINS];
+  __shared__ int wsum[ORD_THREADS / 64];
+  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = item_count[bg];
+  const int4* it = items + (size_t)bg * max_items;
+  const int32_t* lst = list + (size_t)bg * W * K;
+  int32_t* ord = order + (size_t)bg * max_items;
+  int shift = 0;
+  while ((W >> shift) > ORD_BINS) ++shift;
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += ORD_THREADS) atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1);
+  __syncthreads();
+  const int own = cnt[tid];
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  cnt[tid] = incl - own;  // first position of bucket tid
+  __syncthreads();
+  for (int i = tid; i < n; i += ORD_THREADS)
+    ord[atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1)] = i;
+}
+
 template <int D, int R>
 static hipError_t bwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* dout, const float* lse, const float* Dd, const InvBufs& ib,
                                  uint16_t* dq_part, float* dk_acc, float* dv_acc, hipStream_t st) {
   if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  k_item_order<<<g.B * g.G, ORD_THREADS, 0, st>>>(ib.items, ib.item_count, ib.list, ib.order, ib.max_items, g.K,
+                                                  w.W);
   dim3 grid(ib.max_items * g.B * g.G), block(BWD_THREADS);
-  k_bwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, dout, lse, Dd, ib.items, ib.item_count, ib.list, dq_part, dk_acc,
-                                         dv_acc, g.T, g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale,
+  k_bwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, dout, lse, Dd, ib.items, ib.item_count, ib.list, ib.order, dq_part,
+                                         dk_acc, dv_acc, g.T, g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale,
                                          g.scale * LOG2E);
   return hipGetLastError();
 }

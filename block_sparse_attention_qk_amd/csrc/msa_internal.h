@@ -47,6 +47,7 @@ struct InvBufs {
   int4* items;          // [BG][max_items]  {block, start, len, ITEM_* flags}
   int32_t* item_count;  // [BG]
   int32_t* list;        // [BG][W * K]  entries (t - t0) << LIST_SLOT_BITS | slot
+  int32_t* order;       // [BG][max_items]  backward dispatch order of the items (by first token)
   int max_items;
 };
 int inv_max_items(const Geo& g, int W, int item_tokens);
