@@ -498,50 +498,12 @@ __global__ __launch_bounds__(256) void k_cvt_bf16(const float4* __restrict__ src
   }
 }
 
-// Dispatch order of a (batch, group)'s backward items: by the first token of
-// their run (a counting sort into ORD_BINS token buckets), so that the items
-// running at one time gather query and dO rows from a narrow token range.
-constexpr int ORD_THREADS = 1024, ORD_BINS = 1024;
-__global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restrict__ items,
-                                                           const int32_t* __restrict__ item_count,
-                                                           const int32_t* __restrict__ list, int32_t* __restrict__ order,
-                                                           int max_items, int K, int W) {
-  __shared__ int cnt[ORD_BINS];
-  __shared__ int wsum[ORD_THREADS / 64];
-  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = item_count[bg];
-  const int4* it = items + (size_t)bg * max_items;
-  const int32_t* lst = list + (size_t)bg * W * K;
-  int32_t* ord = order + (size_t)bg * max_items;
-  int shift = 0;
-  while ((W >> shift) > ORD_BINS) ++shift;
-  cnt[tid] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += ORD_THREADS) atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1);
-  __syncthreads();
-  const int own = cnt[tid];
-  int incl = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  for (int w = 0; w < wave; ++w) incl += wsum[w];
-  cnt[tid] = incl - own;  // first position of bucket tid
-  __syncthreads();
-  for (int i = tid; i < n; i += ORD_THREADS)
-    ord[atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1)] = i;
-}
-
 template <int D, int R>
 static hipError_t bwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* dout, const float* lse, const float* Dd, const InvBufs& ib,
                                  uint16_t* dq_part, float* dk_acc, float* dv_acc, hipStream_t st) {
   if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  k_item_order<<<g.B * g.G, ORD_THREADS, 0, st>>>(ib.items, ib.item_count, ib.list, ib.order, ib.max_items, g.K,
-                                                  w.W);
+  if (const hipError_t e = launch_item_order(g, w, ib, st); e != hipSuccess) return e;
   dim3 grid(ib.max_items * g.B * g.G), block(BWD_THREADS);
   k_bwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, dout, lse, Dd, ib.items, ib.item_count, ib.list, ib.order, dq_part,
                                          dk_acc, dv_acc, g.T, g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale,

@@ -57,6 +57,8 @@ hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const 
 // 1 if a row has an entry that is neither -1 nor a causal block, a repeated
 // block, or no block at all.
 hipError_t launch_check_idx(const Geo& g, const int32_t* idx, int32_t* flag, hipStream_t st);
+// Dispatch order of ib's items (ib.order): by the first token of each item's run.
+hipError_t launch_item_order(const Geo& g, const Win& w, const InvBufs& ib, hipStream_t st);
 // Work items {block, start, len, split} of the inverse index already built in
 // `ib` (counts/len/base/list), cut at another item size into ib's items buffer.
 hipError_t launch_inverse_items(const Geo& g, const InvBufs& ib, int item_tokens, hipStream_t st);

@@ -186,6 +186,49 @@ hipError_t launch_check_idx(const Geo& g, const int32_t* idx, int32_t* flag, hip
   return hipGetLastError();
 }
 
+// Dispatch order of a (batch, group)'s work items: by the first token of
+// their run (a counting sort into ORD_BINS token buckets), so that the items
+// running at one time gather query rows from a narrow token range.  Items of
+// one bucket keep no particular order among themselves.
+constexpr int ORD_THREADS = 1024, ORD_BINS = 1024;
+__global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restrict__ items,
+                                                           const int32_t* __restrict__ item_count,
+                                                           const int32_t* __restrict__ list, int32_t* __restrict__ order,
+                                                           int max_items, int K, int W) {
+  __shared__ int cnt[ORD_BINS];
+  __shared__ int wsum[ORD_THREADS / 64];
+  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = item_count[bg];
+  const int4* it = items + (size_t)bg * max_items;
+  const int32_t* lst = list + (size_t)bg * W * K;
+  int32_t* ord = order + (size_t)bg * max_items;
+  int shift = 0;
+  while ((W >> shift) > ORD_BINS) ++shift;
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += ORD_THREADS) atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1);
+  __syncthreads();
+  const int own = cnt[tid];
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wsum[w];
+  cnt[tid] = incl - own;  // first position of bucket tid
+  __syncthreads();
+  for (int i = tid; i < n; i += ORD_THREADS)
+    ord[atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1)] = i;
+}
+
+hipError_t launch_item_order(const Geo& g, const Win& w, const InvBufs& ib, hipStream_t st) {
+  k_item_order<<<g.B * g.G, ORD_THREADS, 0, st>>>(ib.items, ib.item_count, ib.list, ib.order, ib.max_items, g.K, w.W);
+  return hipGetLastError();
+}
+
 int inv_max_items(const Geo& g, int W, int item_tokens) {
   const long long pairs = (long long)W * g.K;
   long long m = g.N + pairs / item_tokens + 1;
