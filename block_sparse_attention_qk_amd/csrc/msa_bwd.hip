@@ -10,9 +10,9 @@
 //     S = Q K^T and dP = dO V^T (32 rows x its 32 keys; K, V rows in registers),
 //     P = exp(scale S - LSE) (zero past the query), dS = scale P (dP - D),
 //     P^T and dS^T -> LDS; and they gather the query rows of tile i+3.
-//   consumers (waves 4-7), key quarter kq: for tile i,
-//     dV += P^T dO, dK += dS^T Q   (its 32 keys x the whole head dim),
-//     dQ^T = K^T dS^T               (head-dim tile kq x the 32 rows),
+//   consumers (waves 4-7), cw = wave - 4: for tile i,
+//     dV += P^T dO, dK += dS^T Q   (key half cw/2 x head-dim half cw%2),
+//     dQ^T = K^T dS^T               (head-dim tile cw x the 32 rows),
 //   one barrier per tile.  Query tiles (32 rows = 32/R tokens x R heads) are
 // triple-buffered in LDS, P^T/dS^T double-buffered; every LDS tile is
 // XOR-swizzled on 16-byte chunks (v_mfma_f32_32x32x16_bf16 operands by 16-byte
@@ -275,9 +275,17 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
     }
   } else {
     // =================== consumer ===================
-    f32x16 dka[NCT], dva[NCT];
+    // Consumer cw = wave - 4 owns keys 64kh .. 64kh+63 (two 32-key tiles kt)
+    // and head-dim tiles NCC dh .. NCC dh + NCC - 1 of dV and dK: each P^T/dS^T
+    // operand read feeds NCC MFMAs (its dim tiles) and each dO/Q operand read
+    // two (both key tiles).
+    constexpr int NCC = NCT / 2;  // head-dim tiles per consumer
+    const int cw = wave - 4, kh = cw >> 1, dh = cw & 1;
+    f32x16 dka[2][NCC], dva[2][NCC];
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) dka[c] = dva[c] = zero16();
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) dka[kt][cc] = dva[kt][cc] = zero16();
     __syncthreads();  // K block and tile 0 staged
 
     // One tile: the buffer indices are compile-time constants in each copy of
@@ -288,21 +296,31 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       if (i >= 0 && i < ntiles) {
         const bf16raw* Qc = Qs[qb];
         const bf16raw* dOc = dOs[qb];
-        // ---- dV += P^T dO, dK += dS^T Q : own keys x all head-dim tiles, the tile's 32 rows
+        // ---- dV += P^T dO, dK += dS^T Q : own 64 keys x own 64 head dims, the tile's 32 rows
 #pragma unroll
         for (int st = 0; st < TR / 16; ++st) {
-          const bf16x8 ap = ld8(&PT[pb][kown * TR + 8 * pswz(kown, 2 * st + h)]);
-          const bf16x8 ad = ld8(&dST[pb][kown * TR + 8 * pswz(kown, 2 * st + h)]);
+          bf16x8 ap[2], ad[2];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int key = 64 * kh + 32 * kt + l32;
+            ap[kt] = ld8(&PT[pb][key * TR + 8 * pswz(key, 2 * st + h)]);
+            ad[kt] = ld8(&dST[pb][key * TR + 8 * pswz(key, 2 * st + h)]);
+          }
           const int ra = 16 * st + 8 * h + (i16 >> 2);  // rows of the first transpose read
 #pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            const int col = 32 * c + 16 * g16 + 4 * (i16 & 3);
+          for (int cc = 0; cc < NCC; ++cc) {
+            const int col = 32 * (NCC * dh + cc) + 16 * g16 + 4 * (i16 & 3);
             const int oa = ra * D + 8 * swz<DCH>(ra, col >> 3) + (col & 7);
             const int ob = (ra + 4) * D + 8 * swz<DCH>(ra + 4, col >> 3) + (col & 7);
             const uint2 d0 = lds_tr4(&dOc[oa]), d1 = lds_tr4(&dOc[ob]);
             const uint2 q0 = lds_tr4(&Qc[oa]), q1 = lds_tr4(&Qc[ob]);
-            dva[c] = mfma32(ap, as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y)), dva[c]);
-            dka[c] = mfma32(ad, as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y)), dka[c]);
+            const bf16x8 bd = as_bf8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+            const bf16x8 bq = as_bf8(make_uint4(q0.x, q0.y, q1.x, q1.y));
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              dva[kt][cc] = mfma32(ap[kt], bd, dva[kt][cc]);
+              dka[kt][cc] = mfma32(ad[kt], bq, dka[kt][cc]);
+            }
           }
         }
         // ---- dQ^T tile = K^T dS^T : head-dim tile kq along M, the 32 rows along N, keys as K
@@ -368,38 +386,45 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
       consume(I1{}, I0{}, i0 + 5);
     }
 
-    // ---- dK, dV of the owned keys: lane holds head-dim column 32c + l32, keys 32kq + 8j + 4h + i.
+    // ---- dK, dV of the owned keys and dims: lane holds head-dim column
+    // 32(NCC dh + cc) + l32 of keys 64kh + 32kt + 8j + 4h + i.
+    float* const dkb = dk_acc + kv0 * D;
+    float* const dvb = dv_acc + kv0 * D;
     if (it.w & ITEM_SPLIT) {  // one of several items of this block: they run concurrently, so add atomically
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
-          const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
-          unsafeAtomicAdd(&dk_acc[off], dka[c][e]);
-          unsafeAtomicAdd(&dv_acc[off], dva[c][e]);
-        }
+        for (int cc = 0; cc < NCC; ++cc)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = 64 * kh + 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int off = kk * G * D + 32 * (NCC * dh + cc) + l32;
+            unsafeAtomicAdd(&dkb[off], dka[kt][cc][e]);
+            unsafeAtomicAdd(&dvb[off], dva[kt][cc][e]);
+          }
       return;
     }
-    // The block's only item: per head-dim tile, all 32 accumulator reads are issued before the stores.
+    // The block's only item: per (key tile, dim tile), all 32 accumulator reads are issued before the stores.
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      float ok[16], ov[16];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
-        const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
-        ok[e] = dk_acc[off];
-        ov[e] = dv_acc[off];
+      for (int cc = 0; cc < NCC; ++cc) {
+        float ok[16], ov[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = 64 * kh + 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3);
+          const int off = kk * G * D + 32 * (NCC * dh + cc) + l32;
+          ok[e] = dkb[off];
+          ov[e] = dvb[off];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kk = 64 * kh + 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3);
+          const int off = kk * G * D + 32 * (NCC * dh + cc) + l32;
+          dkb[off] = ok[e] + dka[kt][cc][e];
+          dvb[off] = ov[e] + dva[kt][cc][e];
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = 32 * kq + 8 * (e >> 2) + 4 * h + (e & 3);
-        const size_t off = (kv0 + (size_t)kk * G) * D + 32 * c + l32;
-        dk_acc[off] = ok[e] + dka[c][e];
-        dv_acc[off] = ov[e] + dva[c][e];
-      }
-    }
   }
 }
 
