@@ -17,7 +17,7 @@
 // triple-buffered in LDS, P^T/dS^T double-buffered; every LDS tile is
 // XOR-swizzled on 16-byte chunks (v_mfma_f32_32x32x16_bf16 operands by 16-byte
 // reads and by ds_read_b64_tr_b16 transpose reads).
-// Items are dispatched in the order of their first token.
+// Items are dispatched in the order of the middle token of their run.
 // dQ leaves as one bf16 partial per (token, slot); a combine pass sums a
 // token's partials.  dK/dV are added into fp32 accumulators once per item
 // (atomically only when a block's list is cut into several items).
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void k_bwd_kv(
   __shared__ int lsts[BWD_ITEM_TOKENS];  // the item's pair list
 
   // Groups run one after another in dispatch order, and a group's items in
-  // the order of their first token (k_item_order): the query and dO rows that
+  // the order of their middle token (k_item_order): the query and dO rows that
   // the running items gather then come from one group and a narrow token
   // range, which the last-level cache holds far better than all of a group's
   // rows (items are capped at BWD_ITEM_TOKENS pairs, so no single item

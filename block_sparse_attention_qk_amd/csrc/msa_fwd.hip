@@ -333,7 +333,7 @@ static hipError_t fwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, 
                                  const InvBufs& ib, uint16_t* part_o, float* part_lse, hipStream_t st) {
   if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid(ib.max_items * g.B * g.G), block(256);
-  // Items in the order of their first token when a group's K and V blocks fit
+  // Items in the order of their middle token when a group's K and V blocks fit
   // in half of the 256 MB last-level cache: the running items then gather query
   // rows from a narrow token range, and the blocks they load stay cached.  For
   // larger groups the block order keeps each block's items together instead,

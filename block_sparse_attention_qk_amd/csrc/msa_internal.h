@@ -18,7 +18,7 @@ struct Win {
 };
 
 constexpr int INV_CHUNK = 256;  // tokens per counting-sort chunk
-constexpr int FWD_ITEM_TOKENS = 256;  // tokens per forward work item (list chunk)
+constexpr int FWD_ITEM_TOKENS = 512;  // tokens per forward work item (list chunk)
 // Backward items hold at most this many pairs: a block picked by more tokens
 // (early blocks, or a fixed pattern's far blocks that every query reads) is cut
 // into several items that run in parallel and add their dK/dV atomically.
@@ -47,7 +47,7 @@ struct InvBufs {
   int4* items;          // [BG][max_items]  {block, start, len, ITEM_* flags}
   int32_t* item_count;  // [BG]
   int32_t* list;        // [BG][W * K]  entries (t - t0) << LIST_SLOT_BITS | slot
-  int32_t* order;       // [BG][max_items]  backward dispatch order of the items (by first token)
+  int32_t* order;       // [BG][max_items]  dispatch order of the items (by middle token)
   int max_items;
 };
 int inv_max_items(const Geo& g, int W, int item_tokens);
@@ -57,7 +57,7 @@ hipError_t launch_inverse(const Geo& g, const Win& w, const int32_t* idx, const 
 // 1 if a row has an entry that is neither -1 nor a causal block, a repeated
 // block, or no block at all.
 hipError_t launch_check_idx(const Geo& g, const int32_t* idx, int32_t* flag, hipStream_t st);
-// Dispatch order of ib's items (ib.order): by the first token of each item's run.
+// Dispatch order of ib's items (ib.order): by the middle token of each item's run.
 hipError_t launch_item_order(const Geo& g, const Win& w, const InvBufs& ib, hipStream_t st);
 // Work items {block, start, len, split} of the inverse index already built in
 // `ib` (counts/len/base/list), cut at another item size into ib's items buffer.

@@ -186,10 +186,11 @@ hipError_t launch_check_idx(const Geo& g, const int32_t* idx, int32_t* flag, hip
   return hipGetLastError();
 }
 
-// Dispatch order of a (batch, group)'s work items: by the first token of
-// their run (a counting sort into ORD_BINS token buckets), so that the items
-// running at one time gather query rows from a narrow token range.  Items of
-// one bucket keep no particular order among themselves.
+// Dispatch order of a (batch, group)'s work items: by the middle token of
+// their run (the mean of its first and last token; a counting sort into
+// ORD_BINS token buckets), so that the items running at one time gather query
+// rows from a narrow token range.  Items of one bucket keep no particular
+// order among themselves.
 constexpr int ORD_THREADS = 1024, ORD_BINS = 1024;
 __global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restrict__ items,
                                                            const int32_t* __restrict__ item_count,
@@ -206,7 +207,13 @@ __global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restri
   while ((W >> shift) > ORD_BINS) ++shift;
   cnt[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += ORD_THREADS) atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1);
+  // an item holds at least one pair, so its last entry is start + len - 1
+  auto bucket = [&](int i) {
+    const int4 e = it[i];
+    const int mid = ((lst[e.y] >> LIST_SLOT_BITS) + (lst[e.y + e.z - 1] >> LIST_SLOT_BITS)) / 2;
+    return min(ORD_BINS - 1, mid >> shift);
+  };
+  for (int i = tid; i < n; i += ORD_THREADS) atomicAdd(&cnt[bucket(i)], 1);
   __syncthreads();
   const int own = cnt[tid];
   int incl = own;
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(ORD_THREADS) void k_item_order(const int4* __restri
   cnt[tid] = incl - own;  // first position of bucket tid
   __syncthreads();
   for (int i = tid; i < n; i += ORD_THREADS)
-    ord[atomicAdd(&cnt[min(ORD_BINS - 1, (lst[it[i].y] >> LIST_SLOT_BITS) >> shift)], 1)] = i;
+    ord[atomicAdd(&cnt[bucket(i)], 1)] = i;
 }
 
 hipError_t launch_item_order(const Geo& g, const Win& w, const InvBufs& ib, hipStream_t st) {
