@@ -228,7 +228,7 @@ __global__ __launch_bounds__(DTK_THREADS) void k_dec_topk(const float* __restric
       if (w < wave) eq_before += c;
       eq_total += c;
     }
-    const bool sel = gt || (eq && eq_before + __popcll(meq & lt) < need_eq);
+    const bool sel = gt || (eq && eq_before + (int)__popcll(meq & lt) < need_eq);
     const unsigned long long msel = __ballot(sel);
     if (lane == 0) red[1][wave] = (uint32_t)__popcll(msel);
     __syncthreads();

@@ -50,12 +50,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd_kv(const bf16raw* __restrict__ q
   // Groups run one after another in dispatch order (items are short, so the
   // order does not unbalance the launch): the Q rows the running items re-read
   // are one group's, a quarter of Q at G = 4, which stays in the last-level cache.
-  // Within a group, items run in block order, or in the order of their first
-  // token when `order` is given.
+  // Within a group, items run in the order of their middle token (k_item_order).
   const int BG = (int)gridDim.x / max_items;
   const int bg = (int)blockIdx.x / max_items, slot = (int)blockIdx.x % max_items;
   if (slot >= item_count[bg]) return;
-  const int item = order != nullptr ? order[(size_t)bg * max_items + slot] : slot;
+  const int item = order[(size_t)bg * max_items + slot];
   const int4 it = items[(size_t)bg * max_items + item];
   const int blk = it.x, start = it.y, len = it.z;
   const int b = bg / G, g = bg % G;
@@ -333,17 +332,11 @@ static hipError_t fwd_partials_t(const Geo& g, const Win& w, const uint16_t* q, 
                                  const InvBufs& ib, uint16_t* part_o, float* part_lse, hipStream_t st) {
   if ((long long)ib.max_items * g.B * g.G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid(ib.max_items * g.B * g.G), block(256);
-  // Items in the order of their middle token when a group's K and V blocks fit
-  // in half of the 256 MB last-level cache: the running items then gather query
-  // rows from a narrow token range, and the blocks they load stay cached.  For
-  // larger groups the block order keeps each block's items together instead,
-  // and with them its K/V loads.
-  const int32_t* order = nullptr;
-  if ((size_t)g.N * BLK * g.D * 2 * 2 <= ((size_t)128 << 20)) {
-    if (const hipError_t e = launch_item_order(g, w, ib, st); e != hipSuccess) return e;
-    order = ib.order;
-  }
-  k_fwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, ib.items, ib.item_count, ib.list, order, part_o, part_lse, g.T,
+  // Items in the order of their middle token: the running items then gather
+  // query rows from a narrow token range, which the L2 and the last-level cache
+  // serve far better than rows spread over the whole window.
+  if (const hipError_t e = launch_item_order(g, w, ib, st); e != hipSuccess) return e;
+  k_fwd_kv<D, R><<<grid, block, 0, st>>>(q, k, v, ib.items, ib.item_count, ib.list, ib.order, part_o, part_lse, g.T,
                                          g.H, g.G, g.K, w.t0, w.W, ib.max_items, g.scale, g.scale * LOG2E);
   return hipGetLastError();
 }

@@ -45,7 +45,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // by global-to-LDS copies issued two blocks ahead; pooled values collect in a
 // double-buffered LDS table and leave as 32-byte row segments.
 template <int DP>
-__global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw* __restrict__ qp,
+__global__ __launch_bounds__(64 * POOL_WAVES, DP <= 64 ? 4 : 2) void k_proxy_pool(const bf16raw* __restrict__ qp,
                                                        const bf16raw* __restrict__ kp,
                                                        float* __restrict__ pooled, int T, int G, int N,
                                                        int t0, int W) {
@@ -55,6 +55,7 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
   constexpr int PST = POOL_CHB + 1;    // pooled table row stride (floats)
   // three ring slots as separate arrays: with the slot of every access known at
   // compile time, the copies into one slot are seen not to alias reads of another
+  static_assert(POOL_NBUF == 3, "the ring is the three arrays below");
   __shared__ __attribute__((aligned(16))) bf16raw kslot0[BLK * DP];
   __shared__ __attribute__((aligned(16))) bf16raw kslot1[BLK * DP];
   __shared__ __attribute__((aligned(16))) bf16raw kslot2[BLK * DP];
@@ -112,13 +113,13 @@ __global__ __launch_bounds__(64 * POOL_WAVES, 4) void k_proxy_pool(const bf16raw
     }
   };
 
-  // One key block: block kb is in slot SL, the copy of block kb+2 goes to slot (SL+2)%3.
+  // One key block: block kb is in slot SL, the copy of block kb+2 goes to slot (SL+2) % POOL_NBUF.
   auto step = [&](auto sl, int kb) {
     constexpr int SL = decltype(sl)::value;
     // a finished chunk of pooled values leaves first, so that its stores are
     // older than this step's copy and never held up by the wait below
     if (kb > 0 && kb % POOL_CHB == 0) flush(kb / POOL_CHB - 1);
-    dma(kb + 2, slot_ptr(std::integral_constant<int, (SL + 2) % 3>{}));  // slot of block kb-1: finished
+    dma(kb + 2, slot_ptr(std::integral_constant<int, (SL + 2) % POOL_NBUF>{}));  // slot of block kb-1: finished
 
     const bf16raw* kc = slot_ptr(sl);
     const bool need_mask = kb * BLK + BLK - 1 > qt0 + 32 * wave;  // keys past some query of this wave
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(TKW_THREADS) void k_topk_wg(const float* __restrict
     const int gt_before = (int)(excl & 0xffffu), eq_before = (int)(excl >> 16);
     const int take = need_eq - eq_before;  // equal keys of this word still wanted
     uint32_t ek = 0u;
-    if (take >= __popc(ew)) {
+    if (take >= (int)__popc(ew)) {
       ek = ew;
     } else if (take > 0) {  // the lowest `take` set bits
       uint32_t r = ew;

@@ -334,6 +334,34 @@ def test_long_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
 
 
+@pytest.mark.parametrize("T,topk,big", [(1 << 18, 40, 1500), (1 << 20, 288, 6000)])
+def test_long_rows_surplus_ties_keep_a_later_larger_block(msa, oracle_mod, T, topk, big):
+    """Rows longer than 1024 blocks whose k-th score is shared by more blocks
+    than are needed, with one strictly larger block far after them: every
+    complete block repeats one 128-row proxy-key block (equal pooled scores),
+    and block `big` holds those keys times 4 (with positive proxy queries its
+    pooled score is exactly 4 times the tied one).  The larger block must be
+    chosen, and the remaining slots go to the lowest tied blocks: a word of the
+    write-out bitmap that comes after the last needed tied block takes none of
+    its tied blocks."""
+    print("long-row surplus ties", T, topk, big, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(37)
+    base = torch.randn((128, G, dp), generator=g)
+    kp = base.repeat(T // 128, 1, 1).unsqueeze(0).contiguous()
+    kp[0, big * 128:(big + 1) * 128] *= 4.0
+    kp = kp.to(torch.bfloat16)
+    qp = (torch.rand((1, T, G, dp), generator=g) + 0.5).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([T - 1, T - 200, (big + 1) * 128 + 5, (big + 1) * 128 - 1, big * 128 - 1, 1100 * 128 + 3])
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    assert all(big in r for r in idx_ref[:3, 0, :].tolist())  # the case this test is about
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
 @pytest.mark.parametrize("T,topk", [(1 << 14, 16), (1 << 17, 32)])
 def test_short_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     """Rows of at most 1024 blocks go through one wave per row.  With one
