@@ -98,6 +98,32 @@ def test_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     assert list(idx_ref[0, 0]) == list(range(topk))
 
 
+@pytest.mark.parametrize("T,topk", [(1 << 17, 32), (1 << 20, 300)])
+def test_few_distinct_scores_match_oracle(msa, oracle_mod, T, topk):
+    """Every complete block repeats one 128-row proxy-key block scaled by 16, 8,
+    4 or 1; with positive proxy queries the pooled scores take those four
+    values times one maximum, exactly.  About k/2 blocks are scaled by 16 and a
+    third by 8, so the k-th score is an 8 shared by far more blocks than are
+    needed, with 16s on both sides of the needed ones: the chosen blocks must
+    match the oracle's lowest-index-first choice bit for bit."""
+    print("decode few distinct scores", T, topk, flush=True)
+    G, dp, B = 1, 32, 2
+    g = torch.Generator().manual_seed(43)
+    N = T // 128
+    base = torch.randn((128, G, dp), generator=g)
+    u = torch.rand((B, N), generator=g)
+    scale = torch.where(u < 0.5 * topk / N, 16.0, torch.where(u < 0.33, 8.0, torch.where(u < 0.66, 4.0, 1.0)))
+    kp = (base.repeat(N, 1, 1)[None] * scale.repeat_interleave(128, dim=1)[:, :, None, None]).contiguous()
+    kp = kp.to(torch.bfloat16)
+    qp = (torch.rand((B, G, dp), generator=g) + 0.5).to(torch.bfloat16)
+    lens = [T - 3, T // 2 + 100]
+    idx = msa.msa_decode_select(qp.cuda(), kp.cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"), topk)
+    torch.cuda.synchronize()
+    dm = Dims(B, T, 1, G, 64, dp, topk)
+    idx_ref, _ = oracle_mod.decode_select(dm, qp, kp, lens)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+
+
 def test_decode_rows_equal_training_rows(msa, oracle_mod):
     """A decode step over a sequence's caches gives that sequence's training row."""
     cfg = synth.custom(2, 4096, 32, 4, 128, 64, 8)

@@ -362,6 +362,38 @@ def test_long_rows_surplus_ties_keep_a_later_larger_block(msa, oracle_mod, T, to
     np.testing.assert_array_equal(got, idx_ref[:, 0, :])
 
 
+@pytest.mark.parametrize("T,topk", [(1 << 17, 32), (1 << 18, 40), (1 << 20, 288)])
+def test_few_distinct_scores_match_oracle(msa, oracle_mod, T, topk):
+    """Pooled scores that take only four values, in random block order: every
+    complete block repeats one 128-row proxy-key block scaled by 16, 8, 4 or 1
+    (with positive proxy queries a block's pooled score is that power of two
+    times the same maximum, exactly).  About k/2 blocks of a full row are
+    scaled by 16 and a third by 8, so the k-th score is an 8 shared by far more
+    blocks than are needed, with 16s before and after the needed ones in every
+    part of the row: rows of up to 1024 blocks (one wave per row) and of 2048
+    and 8192 blocks (a workgroup per row) must match the oracle's
+    lowest-index-first choice bit for bit."""
+    print("few distinct scores", T, topk, flush=True)
+    G, dp = 1, 32
+    g = torch.Generator().manual_seed(41)
+    N = T // 128
+    base = torch.randn((128, G, dp), generator=g)
+    u = torch.rand((N,), generator=g)
+    scale = torch.where(u < 0.5 * topk / N, 16.0, torch.where(u < 0.33, 8.0, torch.where(u < 0.66, 4.0, 1.0)))
+    kp = (base.repeat(N, 1, 1) * scale.repeat_interleave(128)[:, None, None]).unsqueeze(0).contiguous()
+    kp = kp.to(torch.bfloat16)
+    qp = (torch.rand((1, T, G, dp), generator=g) + 0.5).to(torch.bfloat16)
+    idx = msa.msa_proxy_select(qp.cuda(), kp.cuda(), topk)
+    torch.cuda.synchronize()
+    rows = np.array([T - 1, T - 129, T // 2 + 5, T // 3 + 77, 1100 * 128 + 1, 700 * 128 + 127, 40 * 128 + 64,
+                     topk * 128 + 3])
+    rows = rows[rows < T]
+    dm = Dims(1, T, G, G, 64, dp, topk)
+    idx_ref = oracle_mod.select(dm, qp, kp, rows=rows)
+    got = idx[0, 0].cpu().numpy()[rows]
+    np.testing.assert_array_equal(got, idx_ref[:, 0, :])
+
+
 @pytest.mark.parametrize("T,topk", [(1 << 14, 16), (1 << 17, 32)])
 def test_short_rows_equal_scores_take_the_lower_blocks(msa, oracle_mod, T, topk):
     """Rows of at most 1024 blocks go through one wave per row.  With one
