@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256) void k_dq_combine(const int32_t* __restrict__ 
     for (int u = 0; u < SB; ++u) {
       const int s = min(s0 + u, K - 1);
       ent[u] = ir[s];
-      raw[u] = ld16u(pp + (size_t)s * R * D);
+      raw[u] = ld16nt(pp + (size_t)s * R * D);
     }
     // keep every load above the masking (the compiler would otherwise sink one
     // into a branch and issue it after the rest, costing a second round trip)

@@ -85,6 +85,13 @@ __device__ __forceinline__ void st16nt(void* p, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
+// 16-byte load marked non-temporal, for streams read exactly once (the
+// partials in the combines, the proxy-key cache in decode): their lines are
+// not kept, so they do not displace data that is read again.
+__device__ __forceinline__ uint4 ld16nt(const void* p) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 __device__ __forceinline__ bf16x8 as_bf8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Transposing two 8-element rows a, b (as 4 words each) into 8 words of

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void k_dec_pool(const bf16raw* __re
   for (int i0 = 0; i0 < LOADS; i0 += U) {
     uint4 r[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = ld16u(src + (size_t)min((i0 + u) * TPL + tok, jmax) * rs);
+    for (int u = 0; u < U; ++u) r[u] = ld16nt(src + (size_t)min((i0 + u) * TPL + tok, jmax) * rs);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float s = dot8(q, r[u]);

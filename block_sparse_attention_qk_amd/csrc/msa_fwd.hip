@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const int32_t* __restrict__
       const int s = min(s0 + u, K - 1);
       ent[u] = ir[s];
       lv[u] = pl[(size_t)s * R];
-      raw[u] = ld16u(po + (size_t)s * R * D);
+      raw[u] = ld16nt(po + (size_t)s * R * D);
     }
     // keep every load above the masking (the compiler would otherwise sink one
     // into a branch and issue it after the rest, costing a second round trip)
