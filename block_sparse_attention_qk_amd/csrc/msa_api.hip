@@ -21,7 +21,10 @@ constexpr size_t ALIGN = 256;
 // per selected block, and the last-level cache then serves most re-reads.
 constexpr size_t FWD_WINDOW_Q_BYTES = (size_t)64 << 20;
 constexpr size_t CAP_SELECT = (size_t)8 << 30;
-constexpr size_t CAP_MAIN = (size_t)40 << 30;
+// The Main Branch workspace a call asks for: one MI355X holds 288 GB, and fewer,
+// longer windows (1M: 15 instead of 31 at half this size) cut launch tails
+// and inverse-index rebuilds.
+constexpr size_t CAP_MAIN = (size_t)80 << 30;
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
