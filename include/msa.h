@@ -105,8 +105,9 @@ typedef enum {
  * MSA_OP_SELECT and MSA_OP_BWD; for MSA_OP_FWD and MSA_OP_FWD_BWD, windows
  * whose query rows of one KV group span at most 64 MiB (32768 tokens at
  * R = 8, d = 128), which keeps the forward's re-reads of those rows in the
- * last-level cache.  Capped at a few tens of GiB for the largest shapes,
- * which are then walked in smaller windows.  Returns 0 for invalid dims. */
+ * last-level cache.  Capped at 80 GiB (8 GiB for MSA_OP_SELECT) for the
+ * largest shapes, which are then walked in smaller windows.  Returns 0 for
+ * invalid dims. */
 size_t msa_workspace_bytes(const msa_dims* dims, msa_op op);
 
 /* Smallest workspace `op` accepts (one 128-token window).  0 for invalid dims. */
